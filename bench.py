@@ -1,0 +1,245 @@
+"""Benchmark: one step = route -> dispatch send -> dispatch recv -> combine on
+one MI355X, over one batch of the DeepSeek-V3-shaped prefill share
+(T=8192 tokens, H=7168, E=256, k=8, 32 virtual ranks x 8 local experts,
+capacity T*k) unless --config names another workload.
+
+Prints ONE JSON line: whole-step tokens/s, the per-kernel breakdown with
+HIP-event durations on the launch stream, the HBM roofline of the dominant
+kernel, and the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--config dsv3_prefill]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of peak), 1 MI355X"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD public spec
+SRC = os.path.join(ROOT, "combine_topk_route_amd", "csrc", "moe_route.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dsv3_prefill.txt")
+
+
+def algorithmic_bytes(cfg) -> dict:
+    """Bytes each entry point must move: every row read or written once."""
+    T, H, E, k, R = cfg.T, cfg.H, cfg.E, cfg.k, cfg.R
+    P = T * k
+    return {
+        "route": 4 * T * E + 8 * P,
+        "dispatch_send": 4 * P + 8 * P + 4 * E + 4 * (E + 1) + 4 * (R + 1),
+        "dispatch_recv": 2 * T * H + 2 * P * H + 4 * P,
+        "combine": 2 * P * H + 2 * T * H + 8 * P,
+    }
+
+
+def source_hash() -> str:
+    with open(SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when there are none or the kernel source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.loads(f.read().split("JSON:", 1)[1].strip().splitlines()[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_hash():
+        return None
+    return rec.get("kernels", {}).get(kernel)
+
+
+def cpu_baseline(cfg_name: str, sample_tokens: int, seed: int) -> dict:
+    import numpy as np  # noqa: F401
+
+    import oracle
+    import workloads
+
+    wl = workloads.make(cfg_name, seed=seed, T=sample_tokens)
+    cfg = wl.cfg
+    t0 = time.perf_counter()
+    idx, _, w32 = oracle.route_topk(wl.logits, cfg.k)
+    counts = oracle.expert_counts(idx, cfg.E)
+    oracle.expert_offsets(counts)
+    pr, _ = oracle.dispatch_slots(idx, cfg.E)
+    oracle.dispatch_rows(wl.x, pr, sample_tokens * cfg.k)
+    oracle.combine(wl.y, pr, w32)
+    dt = time.perf_counter() - t0
+    return {
+        "value": sample_tokens / dt,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"first {sample_tokens} of {cfg.T} tokens of {cfg_name} (same seed and "
+                   f"distribution), route+dispatch+combine in numpy, {dt:.1f} s, "
+                   f"host has {os.cpu_count()} cpus, affinity {len(os.sched_getaffinity(0))}"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="dsv3_prefill")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import combine_topk_route_amd as m
+    import workloads
+
+    cfg = workloads.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workloads.make(cfg, seed=args.seed)
+    T, H, E, k, R = cfg.T, cfg.H, cfg.E, cfg.k, cfg.R
+    P = T * k
+
+    logits = torch.from_numpy(wl.logits).to(dev)
+    x = torch.from_numpy(wl.x.view(np.int16)).view(torch.bfloat16).to(dev)
+    y = torch.from_numpy(wl.y.view(np.int16)).view(torch.bfloat16).to(dev)
+    del wl
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    pair_row = torch.empty((T, k), dtype=torch.int32, device=dev)
+    row_token = torch.empty((P,), dtype=torch.int32, device=dev)
+    rank_off = torch.empty((R + 1,), dtype=torch.int32, device=dev)
+    ws = torch.empty((max(1, m.moe_dispatch_workspace_bytes(T, E, k)),), dtype=torch.uint8,
+                     device=dev)
+    buf = torch.empty((P, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        m.moe_route_topk(logits, k, topk_idx=idx, topk_w=w, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        m.moe_dispatch_send(idx, E, R, expert_counts=counts, expert_offsets=offsets,
+                            pair_row=pair_row, row_token=row_token, rank_offsets=rank_off,
+                            workspace=ws, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        m.moe_dispatch_recv(x, pair_row, buf=buf, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+        m.moe_combine(y, pair_row, w, out=out, stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_host0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    names = ["route", "dispatch_send", "dispatch_recv", "combine"]
+    per = {n: [] for n in names}
+    for e in evs:
+        for j, n in enumerate(names):
+            per[n].append(e[j].elapsed_time(e[j + 1]))
+    nbytes = algorithmic_bytes(cfg)
+    kernels = {}
+    for n in names:
+        us = 1000.0 * float(np.mean(per[n]))
+        gbps = nbytes[n] / (us * 1e-6) / 1e9
+        kernels[n] = {"us_mean": round(us, 2), "us_p10": round(1000 * float(np.percentile(per[n], 10)), 2),
+                      "us_p90": round(1000 * float(np.percentile(per[n], 90)), 2),
+                      "bytes": nbytes[n], "GBps": round(gbps, 1),
+                      "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    dom = max(["dispatch_recv", "combine"], key=lambda n: kernels[n]["us_mean"])
+    step_bytes = sum(nbytes.values())
+    tokens_per_s = T * args.steps / (total_ms * 1e-3)
+
+    # A plain 1 GiB device copy: the practical bandwidth ceiling, and the
+    # reference kernel of known size for scaling FETCH_SIZE / WRITE_SIZE.
+    copy_gbps = None
+    if True:
+        src = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(5):
+            dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        copy_gbps = 2 * (1 << 30) * 5 / (a.elapsed_time(b) * 1e-3) / 1e9
+        del src, dst
+
+    traffic = measured_traffic(dom)
+    rec = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": T, "H": H, "E": E, "k": k, "virtual_ranks": R,
+                   "local_experts": cfg.L, "capacity": P, "seed": args.seed,
+                   "step": "route+dispatch_send+dispatch_recv+combine",
+                   "accumulate": "fp32", "inputs": "resident in HBM"},
+        "hbm_GBps_step": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "hbm_frac_step": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": {
+            "kernel": dom,
+            "bound": "hbm",
+            "achieved": kernels[dom]["GBps"],
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": kernels[dom]["frac_of_peak"],
+            "traffic": traffic,
+        },
+        "kernels": kernels,
+        "copy_1GiB_GBps": None if copy_gbps is None else round(copy_gbps, 1),
+        "host_wall_s": round(t_host, 3),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg.name, min(args.cpu_sample_tokens, T), args.seed)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,214 @@
+"""Thin torch binding of libmoe_route.so: argument marshalling only.
+
+Every function has the name of the C entry point it calls, checks tensor
+placement / dtype / contiguity, allocates outputs the caller did not pass
+(torch is the device-memory and stream provider), and passes raw pointers
+plus the current HIP stream.  All computation runs in the library's kernels;
+there is no other path.  A non-zero status raises ``MoeError``.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import NamedTuple, Optional
+
+import torch
+
+from . import _lib
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = _lib.load().moe_strerror(status).decode()
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def _check(fn: str, status: int) -> None:
+    if status != _lib.MOE_OK:
+        raise MoeError(fn, status)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: Optional[int] = None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device (cuda/HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _empty(shape, dtype, like: torch.Tensor) -> torch.Tensor:
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+def moe_abi_version() -> int:
+    return int(_lib.load().moe_abi_version())
+
+
+def moe_route_topk(logits: torch.Tensor, k: int, topk_idx: Optional[torch.Tensor] = None,
+                   topk_w: Optional[torch.Tensor] = None, stream=None):
+    """Top-k routing: returns (topk_idx int32 [T,k], topk_w fp32 [T,k])."""
+    lp = _dev(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    if topk_idx is None:
+        topk_idx = _empty((T, k), torch.int32, logits)
+    if topk_w is None:
+        topk_w = _empty((T, k), torch.float32, logits)
+    ip = _dev(topk_idx, "topk_idx", torch.int32)
+    wp = _dev(topk_w, "topk_w", torch.float32)
+    if topk_idx.numel() != T * k or topk_w.numel() != T * k:
+        raise ValueError("topk_idx / topk_w must hold T*k elements")
+    _check("moe_route_topk", _lib.load().moe_route_topk(lp, T, E, k, ip, wp, _stream(stream)))
+    return topk_idx, topk_w
+
+
+def moe_dispatch_workspace_bytes(T: int, E: int, k: int) -> int:
+    return int(_lib.load().moe_dispatch_workspace_bytes(T, E, k))
+
+
+class SendResult(NamedTuple):
+    expert_counts: torch.Tensor   # int32 [E]
+    expert_offsets: torch.Tensor  # int32 [E+1]
+    pair_row: torch.Tensor        # int32 [T, k]
+    row_token: torch.Tensor       # int32 [T*k]
+    rank_offsets: Optional[torch.Tensor]  # int32 [R+1]
+
+
+def _send_outputs(topk_idx, E, R, expert_counts, expert_offsets, pair_row, row_token,
+                  rank_offsets, with_rank_offsets):
+    T, k = topk_idx.shape
+    if expert_counts is None:
+        expert_counts = _empty((E,), torch.int32, topk_idx)
+    if expert_offsets is None:
+        expert_offsets = _empty((E + 1,), torch.int32, topk_idx)
+    if pair_row is None:
+        pair_row = _empty((T, k), torch.int32, topk_idx)
+    if row_token is None:
+        row_token = _empty((T * k,), torch.int32, topk_idx)
+    if rank_offsets is None and with_rank_offsets:
+        rank_offsets = _empty((R + 1,), torch.int32, topk_idx)
+    sizes = [(expert_counts, E), (expert_offsets, E + 1), (pair_row, T * k), (row_token, T * k)]
+    if rank_offsets is not None:
+        sizes.append((rank_offsets, R + 1))
+    for t, n in sizes:
+        if t.numel() != n:
+            raise ValueError("dispatch output has the wrong number of elements")
+    return SendResult(expert_counts, expert_offsets, pair_row, row_token, rank_offsets)
+
+
+def _workspace(T, E, k, workspace, like):
+    need = moe_dispatch_workspace_bytes(T, E, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=like.device)
+    if workspace is None:
+        return 0, 0, None
+    return _dev(workspace, "workspace", torch.uint8), workspace.numel(), workspace
+
+
+def moe_dispatch_send(topk_idx: torch.Tensor, E: int, num_vranks: int = 1, *,
+                      expert_counts=None, expert_offsets=None, pair_row=None, row_token=None,
+                      rank_offsets=None, with_rank_offsets: bool = True, workspace=None,
+                      stream=None) -> SendResult:
+    """Counts, offsets and the stable destination row of every (token, j) pair."""
+    ip = _dev(topk_idx, "topk_idx", torch.int32, 2)
+    T, k = topk_idx.shape
+    out = _send_outputs(topk_idx, E, num_vranks, expert_counts, expert_offsets, pair_row,
+                        row_token, rank_offsets, with_rank_offsets)
+    wp, wn, _ = _workspace(T, E, k, workspace, topk_idx)
+    rp = _dev(out.rank_offsets, "rank_offsets", torch.int32) if out.rank_offsets is not None else None
+    _check("moe_dispatch_send", _lib.load().moe_dispatch_send(
+        ip, T, E, k, num_vranks,
+        _dev(out.expert_counts, "expert_counts", torch.int32),
+        _dev(out.expert_offsets, "expert_offsets", torch.int32),
+        _dev(out.pair_row, "pair_row", torch.int32),
+        _dev(out.row_token, "row_token", torch.int32), rp, wp, wn, _stream(stream)))
+    return out
+
+
+def moe_dispatch_recv(x: torch.Tensor, pair_row: torch.Tensor, buf: Optional[torch.Tensor] = None,
+                      capacity: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Scatter bf16 token rows into the expert-major buffer [capacity, H]."""
+    xp = _dev(x, "x", torch.bfloat16, 2)
+    T, H = x.shape
+    k = pair_row.shape[1] if pair_row.dim() == 2 else 0
+    if pair_row.dim() != 2 or pair_row.shape[0] != T:
+        raise ValueError("pair_row must be [T, k]")
+    if buf is None:
+        buf = _empty((T * k if capacity is None else capacity, H), torch.bfloat16, x)
+    if capacity is None:
+        capacity = buf.shape[0]
+    if buf.dim() != 2 or buf.shape[1] != H or buf.shape[0] < capacity:
+        raise ValueError("buf must be [>= capacity, H]")
+    _check("moe_dispatch_recv", _lib.load().moe_dispatch_recv(
+        xp, _dev(pair_row, "pair_row", torch.int32), T, H, k,
+        _dev(buf, "buf", torch.bfloat16), capacity, _stream(stream)))
+    return buf
+
+
+def moe_dispatch(topk_idx: torch.Tensor, x: torch.Tensor, E: int, num_vranks: int = 1, *,
+                 buf=None, capacity=None, expert_counts=None, expert_offsets=None, pair_row=None,
+                 row_token=None, rank_offsets=None, with_rank_offsets: bool = True,
+                 workspace=None, stream=None):
+    """Send then receive on one stream; returns (SendResult, buf)."""
+    ip = _dev(topk_idx, "topk_idx", torch.int32, 2)
+    xp = _dev(x, "x", torch.bfloat16, 2)
+    T, k = topk_idx.shape
+    H = x.shape[1]
+    if x.shape[0] != T:
+        raise ValueError("x and topk_idx disagree on T")
+    out = _send_outputs(topk_idx, E, num_vranks, expert_counts, expert_offsets, pair_row,
+                        row_token, rank_offsets, with_rank_offsets)
+    if buf is None:
+        buf = _empty((T * k if capacity is None else capacity, H), torch.bfloat16, x)
+    if capacity is None:
+        capacity = buf.shape[0]
+    if buf.dim() != 2 or buf.shape[1] != H or buf.shape[0] < capacity:
+        raise ValueError("buf must be [>= capacity, H]")
+    wp, wn, _ = _workspace(T, E, k, workspace, topk_idx)
+    rp = _dev(out.rank_offsets, "rank_offsets", torch.int32) if out.rank_offsets is not None else None
+    _check("moe_dispatch", _lib.load().moe_dispatch(
+        ip, xp, T, E, k, H, num_vranks,
+        _dev(out.expert_counts, "expert_counts", torch.int32),
+        _dev(out.expert_offsets, "expert_offsets", torch.int32),
+        _dev(out.pair_row, "pair_row", torch.int32),
+        _dev(out.row_token, "row_token", torch.int32), rp,
+        _dev(buf, "buf", torch.bfloat16), capacity, wp, wn, _stream(stream)))
+    return out, buf
+
+
+def moe_combine(y: torch.Tensor, pair_row: torch.Tensor, topk_w: torch.Tensor,
+                out: Optional[torch.Tensor] = None, capacity: Optional[int] = None,
+                stream=None) -> torch.Tensor:
+    """Router-weighted sum of each token's k expert rows: bf16 [T, H]."""
+    yp = _dev(y, "y", torch.bfloat16, 2)
+    if pair_row.dim() != 2:
+        raise ValueError("pair_row must be [T, k]")
+    T, k = pair_row.shape
+    H = y.shape[1]
+    if topk_w.shape != pair_row.shape:
+        raise ValueError("topk_w must match pair_row's shape")
+    if capacity is None:
+        capacity = y.shape[0]
+    if capacity > y.shape[0]:
+        raise ValueError("capacity exceeds y's rows")
+    if out is None:
+        out = _empty((T, H), torch.bfloat16, y)
+    if out.shape != (T, H):
+        raise ValueError("out must be [T, H]")
+    _check("moe_combine", _lib.load().moe_combine(
+        yp, _dev(pair_row, "pair_row", torch.int32), _dev(topk_w, "topk_w", torch.float32),
+        T, H, k, capacity, _dev(out, "out", torch.bfloat16), _stream(stream)))
+    return out

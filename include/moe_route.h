@@ -1,0 +1,194 @@
+/*
+ * moe_route.h - C ABI of the MI355X (gfx950) MoE top-k route / dispatch /
+ * combine library (libmoe_route.so).
+ *
+ * The operations follow the pages' statement of the problem:
+ *   - "Efficient and portable mixture-of-experts communication":
+ *     sections "Introduction" (router, top-K, weighted average),
+ *     "Dispatch" (per-expert token counts, packing, routing metadata kept
+ *     for combine) and "Combine" (receiver-side weighted sum into tensors
+ *     the caller allocated).
+ *   - "Enabling trillion-parameter models on AWS EFA": sections "Send and
+ *     Receive Buffers" (prefix sum of counts gives per-peer contiguous
+ *     offsets; buffers sized for the worst case) and "Dispatch and Combine"
+ *     (per-expert counts accumulated in one block; send and receive halves
+ *     as separate kernels so other work can overlap them).
+ *   - "Lower latency and higher throughput with multi-node DeepSeek
+ *     deployment": section "MoE Router" (top-K indices and scores per token;
+ *     dense dispatch needs routing aggregated per expert) and "CUDA Graph"
+ *     (no host-side knowledge of routed counts, so launches can be captured).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every data pointer is a DEVICE pointer owned by the caller (for
+ *    instance a torch tensor's data_ptr()).  The library allocates and frees
+ *    nothing and keeps no global state; it is reentrant.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls only enqueue work on it; none synchronises the device or copies
+ *    device -> host.  Stream order is the only synchronisation: results are
+ *    valid once the stream reaches the end of the enqueued work.
+ *  - bf16 crosses the ABI as raw 16-bit storage (IEEE bfloat16 bit patterns).
+ *  - Return value: MOE_OK (0) or a negative MOE_ERR_* code.  On any error
+ *    nothing has been enqueued and no output has been touched, except
+ *    MOE_ERR_HIP, which reports a failed kernel launch (work enqueued before
+ *    the failing launch in the same call may have run).
+ *  - T == 0 is valid: the call returns MOE_OK and enqueues nothing (the
+ *    output pointers may then be NULL).
+ *  - Checked on the host: null pointers (when T > 0), sizes and limits,
+ *    16-byte alignment of bf16 row pointers, capacity >= T*k, workspace size.
+ *    NOT checked (undefined behaviour if violated): that pointers are device
+ *    memory of the stated size and that logits are finite.  Out-of-range
+ *    expert indices and row indices are handled on the device as documented
+ *    per entry point (never an out-of-bounds access).
+ *
+ * Limits: 1 <= E <= 1024; 1 <= k <= min(E, 32); T*k < 2^31;
+ *         H % 8 == 0 and 8 <= H <= 2^20 for bf16 rows (rows move in 16-byte chunks).
+ */
+#ifndef MOE_ROUTE_H
+#define MOE_ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, size or limit out of range     */
+  MOE_ERR_ALIGNMENT = -2,   /* H % 8 != 0 or a bf16 row pointer not 16-B aligned */
+  MOE_ERR_CAPACITY = -3,    /* capacity < T*k: tokens are never dropped      */
+  MOE_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than required       */
+  MOE_ERR_HIP = -5          /* a kernel launch failed (hipLaunchKernel error) */
+};
+
+/* ABI version of the loaded library (== MOE_ABI_VERSION it was built with). */
+int moe_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* moe_strerror(int status);
+
+/*
+ * moe_route_topk - top-k routing of every token (the router of "Efficient and
+ * portable mixture-of-experts communication", section "Introduction"; the
+ * Mixtral special case of "Lower latency and higher throughput with
+ * multi-node DeepSeek deployment", section "MoE Router").
+ *
+ *   logits   [T, E] fp32, row-major: router logits of each token.
+ *   topk_idx [T, k] int32 (out): the k experts with the largest logits,
+ *            in descending order; equal logits go to the lower expert index
+ *            (+0.0 and -0.0 are equal).  Selecting on the logits equals
+ *            selecting on the softmax probabilities, which are strictly
+ *            increasing in the logits.
+ *   topk_w   [T, k] fp32 (out): fp32 softmax over all E logits, then the k
+ *            selected probabilities divided by their sum (sum to 1 up to fp32
+ *            rounding); topk_w[t, j] belongs to topk_idx[t, j].
+ * Errors: MOE_ERR_INVALID_ARG for T < 0, E or k out of range, null pointers.
+ */
+int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,
+                   int32_t* topk_idx, float* topk_w, void* stream);
+
+/*
+ * moe_dispatch_workspace_bytes - device scratch moe_dispatch_send needs for
+ * (T, E, k): per-block per-expert counts for the multi-block scan.  0 means
+ * no workspace is needed (workspace may then be NULL).  Returns 0 as well for
+ * arguments moe_dispatch_send would reject.
+ */
+size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k);
+
+/*
+ * moe_dispatch_send - the "send" half of dispatch: per-expert token counts,
+ * their exclusive scan into offsets, and a destination row for every
+ * (token, j) pair ("Enabling trillion-parameter models on AWS EFA", sections
+ * "Send and Receive Buffers" and "Dispatch and Combine"; "Efficient and
+ * portable mixture-of-experts communication", section "Dispatch").
+ *
+ * The dispatch buffer is expert-major and packed: expert e owns rows
+ * [expert_offsets[e], expert_offsets[e+1]); expert e = r*L + le belongs to
+ * virtual rank r = e / L (L = E / num_vranks), so the buffer reads as
+ * [virtual_rank][local_expert][slot] and rank r's rows are the contiguous
+ * segment [rank_offsets[r], rank_offsets[r+1]).  Inside one expert, rows
+ * follow the ascending flat pair index p = t*k + j (a stable counting sort).
+ *
+ *   topk_idx       [T, k] int32: expert of each pair.  A pair whose index is
+ *                  outside [0, E) is dropped: it is not counted and its
+ *                  pair_row entry is -1 (indices from moe_route_topk are
+ *                  always in range).
+ *   num_vranks     R >= 1 with E % R == 0.
+ *   expert_counts  [E]   int32 (out): pairs routed to each expert.
+ *   expert_offsets [E+1] int32 (out): exclusive scan; [E] = number of
+ *                  counted pairs (T*k when every index is in range).
+ *   pair_row       [T, k] int32 (out): row of pair (t, j) in the buffer.
+ *   row_token      [T*k] int32 (out): token held by each row (entries past
+ *                  expert_offsets[E] are left untouched).
+ *   rank_offsets   [R+1] int32 (out) or NULL.
+ *   workspace      device scratch of >= moe_dispatch_workspace_bytes(T,E,k)
+ *                  bytes (any contents; overwritten); NULL if that is 0.
+ * Errors: MOE_ERR_INVALID_ARG (limits, E % R != 0, null outputs),
+ *         MOE_ERR_WORKSPACE (workspace missing or too small).
+ */
+int moe_dispatch_send(const int32_t* topk_idx, int64_t T, int32_t E, int32_t k,
+                      int32_t num_vranks, int32_t* expert_counts,
+                      int32_t* expert_offsets, int32_t* pair_row,
+                      int32_t* row_token, int32_t* rank_offsets,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_dispatch_recv - the "receive" half of dispatch: copy each token row
+ * into its k rows of the expert-major buffer, so each expert's tokens are
+ * contiguous for the grouped GEMM ("Efficient and portable
+ * mixture-of-experts communication", section "Dispatch"; "Enabling
+ * trillion-parameter models on AWS EFA", section "Dispatch and Combine").
+ *
+ *   x        [T, H] bf16 (16-byte aligned): token activations.
+ *   pair_row [T, k] int32: from moe_dispatch_send.  Entries outside
+ *            [0, capacity) (the -1 of a dropped pair) are skipped.
+ *   buf      [capacity, H] bf16 (out, 16-byte aligned): buf[pair_row[t,j]]
+ *            becomes a bit copy of x[t]; rows no pair maps to are untouched.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_ALIGNMENT, MOE_ERR_CAPACITY
+ *         (capacity < T*k).
+ */
+int moe_dispatch_recv(const void* x, const int32_t* pair_row, int64_t T,
+                      int32_t H, int32_t k, void* buf, int64_t capacity,
+                      void* stream);
+
+/*
+ * moe_dispatch - moe_dispatch_send followed by moe_dispatch_recv on one
+ * stream; arguments are the union of theirs, with the same meaning.  All
+ * arguments of both halves are checked before anything is enqueued.
+ */
+int moe_dispatch(const int32_t* topk_idx, const void* x, int64_t T, int32_t E,
+                 int32_t k, int32_t H, int32_t num_vranks,
+                 int32_t* expert_counts, int32_t* expert_offsets,
+                 int32_t* pair_row, int32_t* row_token, int32_t* rank_offsets,
+                 void* buf, int64_t capacity, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/*
+ * moe_combine - receiver-side weighted sum of each token's k expert-output
+ * rows ("Efficient and portable mixture-of-experts communication", section
+ * "Combine"; accumulation at the receiver as in "Enabling trillion-parameter
+ * models on AWS EFA", section "Evaluation").
+ *
+ *   y        [capacity, H] bf16 (16-byte aligned): expert outputs, one row per
+ *            dispatched row (same order as the dispatch buffer).
+ *   pair_row [T, k] int32: from moe_dispatch_send.  A term whose entry is
+ *            outside [0, capacity) is skipped (acc is left unchanged).
+ *   topk_w   [T, k] fp32: weights from moe_route_topk.
+ *   out      [T, H] bf16 (out, 16-byte aligned, caller-allocated):
+ *            out[t] = bf16_rne(acc), acc = +0.0f, then for j = 0..k-1
+ *            acc = fmaf(topk_w[t,j], y[pair_row[t,j]], acc) in fp32.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_ALIGNMENT, MOE_ERR_CAPACITY.
+ */
+int moe_combine(const void* y, const int32_t* pair_row, const float* topk_w,
+                int64_t T, int32_t H, int32_t k, int64_t capacity, void* out,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTE_H */

@@ -1,0 +1,67 @@
+"""Helpers shared by the GPU tests: host <-> device moves of bf16 bit arrays
+and the tolerances the parity tests use."""
+import numpy as np
+import torch
+
+DEV = torch.device("cuda:0")
+
+# Routing weights: the kernel's fp32 softmax + renormalisation against the
+# float64 oracle.  Rounding budget (units of u = 2^-24): exp <= 2u, softmax
+# division u, selected-sum (compensated) ~2u, final division u; with the
+# probability's own error counted twice (numerator and sum) this stays below
+# 12u, so 16u = 2^-20 relative, plus an absolute floor for fp32 underflow.
+W_REL = 2.0**-20
+W_ABS = 2.0**-126
+
+# Combine: per element |gpu - ref| <= 2^-7 |ref|; +-0 must match as zero.
+OUT_REL = 2.0**-7
+
+
+def dev_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def dev_i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+def dev_bf16(bits):
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def host_bf16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def bf16_vals(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def assert_weights_close(gpu_w, ref_w):
+    g = np.asarray(gpu_w, np.float64)
+    r = np.asarray(ref_w, np.float64)
+    err = np.abs(g - r)
+    bad = err > W_REL * np.abs(r) + W_ABS
+    assert not bad.any(), (
+        f"{bad.sum()} weights out of tolerance; worst rel err "
+        f"{(err / np.maximum(np.abs(r), 1e-300)).max():.3e}")
+    return float((err / np.maximum(np.abs(r), 1e-300)).max())
+
+
+def assert_out_close(gpu_bits, ref_bits, extra_abs=None):
+    """Combine outputs: within 2^-7 relative per element (plus ``extra_abs``,
+    an optional per-element absolute allowance); returns the count of
+    elements that are not bit-identical."""
+    g = bf16_vals(gpu_bits).astype(np.float64)
+    r = bf16_vals(ref_bits).astype(np.float64)
+    tol = OUT_REL * np.abs(r)
+    if extra_abs is not None:
+        tol = tol + extra_abs
+    bad = ~(np.abs(g - r) <= tol)
+    assert not bad.any(), f"{bad.sum()} of {bad.size} combine elements out of tolerance"
+    return int(np.count_nonzero(np.asarray(gpu_bits) != np.asarray(ref_bits)))

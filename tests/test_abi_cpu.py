@@ -1,0 +1,161 @@
+"""C-ABI boundary tests that need no GPU.
+
+The library loads, exports every function include/moe_route.h declares, and
+rejects invalid arguments with the documented status before any HIP call.
+Every call below carries at least one argument the host-side checks reject
+(or T == 0), so nothing is ever enqueued.  The module is skipped where a GPU
+is visible, so that fake pointers can never reach a kernel.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_route.h")
+
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
+                                reason="host-only checks with fake pointers; run without a GPU")
+
+from combine_topk_route_amd import _lib  # noqa: E402
+
+OK, INVALID, ALIGN, CAP, WS, HIP = (_lib.MOE_OK, _lib.MOE_ERR_INVALID_ARG, _lib.MOE_ERR_ALIGNMENT,
+                                    _lib.MOE_ERR_CAPACITY, _lib.MOE_ERR_WORKSPACE, _lib.MOE_ERR_HIP)
+P16 = 0x10000  # a fake, 16-byte aligned address; never dereferenced
+P4 = 0x10004   # 4-byte but not 16-byte aligned
+S = None       # null stream
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_and_binding_declare_the_same_functions():
+    assert declared_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_version_and_strerror(lib):
+    assert lib.moe_abi_version() == 1
+    for code in (OK, INVALID, ALIGN, CAP, WS, HIP, 12345):
+        s = lib.moe_strerror(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert lib.moe_strerror(12345) == b"unknown status"
+
+
+def test_route_rejects_bad_arguments(lib):
+    f = lib.moe_route_topk
+    assert f(P16, -1, 8, 2, P16, P16, S) == INVALID           # T < 0
+    assert f(P16, 4, 0, 1, P16, P16, S) == INVALID            # E < 1
+    assert f(P16, 4, 1025, 2, P16, P16, S) == INVALID         # E > 1024
+    assert f(P16, 4, 8, 0, P16, P16, S) == INVALID            # k < 1
+    assert f(P16, 4, 8, 9, P16, P16, S) == INVALID            # k > E
+    assert f(P16, 4, 64, 33, P16, P16, S) == INVALID          # k > 32
+    assert f(None, 4, 8, 2, P16, P16, S) == INVALID           # null logits
+    assert f(P16, 4, 8, 2, None, P16, S) == INVALID
+    assert f(P16, 4, 8, 2, P16, None, S) == INVALID
+    assert f(P16, 2**30, 8, 2, P16, P16, S) == INVALID        # T*k >= 2^31
+    assert f(P16 + 1, 4, 8, 2, P16, P16, S) == ALIGN          # misaligned fp32
+    assert f(None, 0, 8, 2, None, None, S) == OK              # T == 0 is a no-op
+
+
+def test_workspace_size_function(lib):
+    f = lib.moe_dispatch_workspace_bytes
+    assert f(0, 8, 2) == 0
+    assert f(16, 8, 2) == 0            # small inputs run fused in one block
+    assert f(128, 256, 8) == 0
+    ws = f(8192, 256, 8)
+    assert ws > 0 and ws % 256 == 0
+    assert f(8192, 0, 8) == 0          # rejected shapes report 0
+    assert f(-1, 8, 2) == 0
+
+
+def test_dispatch_send_rejects_bad_arguments(lib):
+    f = lib.moe_dispatch_send
+    ok_ws = lib.moe_dispatch_workspace_bytes(8192, 256, 8)
+    args = lambda **kw: [kw.get("idx", P16), kw.get("T", 8192), kw.get("E", 256), kw.get("k", 8),
+                         kw.get("R", 32), kw.get("counts", P16), kw.get("offsets", P16),
+                         kw.get("pair_row", P16), kw.get("row_token", P16), kw.get("rank", None),
+                         kw.get("ws", P16), kw.get("wsb", ok_ws), S]
+    assert f(*args(R=3)) == INVALID                 # E % R != 0
+    assert f(*args(R=0)) == INVALID
+    assert f(*args(R=512)) == INVALID               # R > E
+    assert f(*args(k=0)) == INVALID
+    assert f(*args(idx=None)) == INVALID
+    assert f(*args(counts=None)) == INVALID
+    assert f(*args(offsets=None)) == INVALID
+    assert f(*args(pair_row=None)) == INVALID
+    assert f(*args(row_token=None)) == INVALID
+    assert f(*args(pair_row=P16 + 2)) == ALIGN
+    assert f(*args(ws=None)) == WS                  # workspace needed but missing
+    assert f(*args(wsb=ok_ws - 1)) == WS            # workspace too small
+    assert f(*args(T=0, idx=None, counts=None, offsets=None, pair_row=None, row_token=None,
+                   ws=None, wsb=0)) == OK
+
+
+def test_dispatch_recv_and_combine_reject_bad_arguments(lib):
+    r = lib.moe_dispatch_recv
+    assert r(P16, P16, 16, 256, 2, P16, 31, S) == CAP          # capacity < T*k
+    assert r(P16, P16, 16, 255, 2, P16, 32, S) == ALIGN        # H % 8 != 0
+    assert r(P16, P16, 16, 0, 2, P16, 32, S) == INVALID        # H < 8
+    assert r(P4, P16, 16, 256, 2, P16, 32, S) == ALIGN         # x not 16-byte aligned
+    assert r(P16, P16, 16, 256, 2, P4, 32, S) == ALIGN         # buf not 16-byte aligned
+    assert r(None, P16, 16, 256, 2, P16, 32, S) == INVALID
+    assert r(P16, None, 16, 256, 2, P16, 32, S) == INVALID
+    assert r(P16, P16, 16, 256, 0, P16, 32, S) == INVALID      # k < 1
+    assert r(P16, P16, -1, 256, 2, P16, 32, S) == INVALID
+    assert r(None, None, 0, 256, 2, None, 0, S) == OK
+
+    c = lib.moe_combine
+    assert c(P16, P16, P16, 16, 256, 2, 31, P16, S) == CAP
+    assert c(P16, P16, P16, 16, 12, 2, 32, P16, S) == ALIGN
+    assert c(P4, P16, P16, 16, 256, 2, 32, P16, S) == ALIGN
+    assert c(P16, P16, P16, 16, 256, 2, 32, P4, S) == ALIGN
+    assert c(P16, None, P16, 16, 256, 2, 32, P16, S) == INVALID
+    assert c(P16, P16, None, 16, 256, 2, 32, P16, S) == INVALID
+    assert c(None, P16, P16, 16, 256, 2, 32, P16, S) == INVALID
+    assert c(P16, P16, P16, 16, 256, 33, 32 * 16, P16, S) == INVALID  # k > 32
+    assert c(None, None, None, 0, 256, 2, 0, None, S) == OK
+
+
+def test_dispatch_checks_both_halves_before_enqueueing(lib):
+    f = lib.moe_dispatch
+    ws = lib.moe_dispatch_workspace_bytes(8192, 256, 8)
+    base = [P16, P16, 8192, 256, 8, 7168, 32, P16, P16, P16, P16, None, P16, 8192 * 8, P16, ws, S]
+    bad_cap = list(base)
+    bad_cap[13] = 8192 * 8 - 1
+    assert f(*bad_cap) == CAP                      # recv half rejected, send never enqueued
+    bad_r = list(base)
+    bad_r[6] = 5
+    assert f(*bad_r) == INVALID
+    bad_ws = list(base)
+    bad_ws[15] = 0
+    assert f(*bad_ws) == WS
+    bad_h = list(base)
+    bad_h[5] = 7170
+    assert f(*bad_h) == ALIGN
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.load()

@@ -1,0 +1,221 @@
+"""GPU edge cases: ties, degenerate shapes, ragged tiles, path switches,
+canaries, determinism, and the identity-expert round trip."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpuhelp import (DEV, assert_out_close, assert_weights_close, dev_bf16, dev_f32, dev_i32,
+                     host, host_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+def _m():
+    import combine_topk_route_amd as m
+
+    return m
+
+
+def _rand_bf16(shape, seed):
+    rng = np.random.default_rng(seed)
+    return workloads.bf16_from_f32(rng.standard_normal(shape).astype(np.float32))
+
+
+def _route_check(logits, k):
+    m = _m()
+    print(f"[edges] route T={logits.shape[0]} E={logits.shape[1]} k={k}", flush=True)
+    idx, w = m.moe_route_topk(dev_f32(logits), k)
+    torch.cuda.synchronize()
+    r_idx, r_w, _ = oracle.route_topk(logits, k)
+    assert np.array_equal(host(idx), r_idx)
+    assert_weights_close(host(w), r_w)
+    return host(idx), host(w)
+
+
+# ------------------------------------------------------------------ routing
+
+def test_route_ties_and_signed_zeros():
+    E = 256
+    logits = np.random.default_rng(1).standard_normal((64, E)).astype(np.float32)
+    logits[0] = 0.25                               # all equal
+    logits[1, :] = -3.0
+    logits[1, 100:120] = 2.0                        # 20 equal values straddle k = 8
+    logits[2, :] = -1.0
+    logits[2, 7], logits[2, 3] = 0.0, -0.0          # +0 / -0 tie
+    logits[3] = np.round(logits[3] * 2) / 2         # many half-integer ties
+    logits[4, ::3] = 1.5                            # ties spread over all lanes
+    idx, w = _route_check(logits, 8)
+    assert idx[0].tolist() == list(range(8))
+    assert idx[1].tolist() == list(range(100, 108))
+    assert idx[2, :2].tolist() == [3, 7]
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 1), (5, 8, 8), (33, 1, 1), (7, 2, 2), (100, 64, 32),
+                                   (129, 1024, 32), (70, 1000, 7), (3, 65, 3), (257, 384, 8)])
+def test_route_shapes(T, E, k):
+    logits = np.random.default_rng(T * E + k).standard_normal((T, E)).astype(np.float32)
+    _route_check(logits, k)
+
+
+def test_route_wide_logit_range():
+    rng = np.random.default_rng(5)
+    logits = (rng.standard_normal((200, 256)) * 20).astype(np.float32)
+    _route_check(logits, 8)
+
+
+# ------------------------------------------------------------------ dispatch send
+
+def _send_check(idx, E, R):
+    m = _m()
+    T, k = idx.shape
+    print(f"[edges] send T={T} k={k} E={E} R={R} (P={T * k})", flush=True)
+    res = m.moe_dispatch_send(dev_i32(idx), E, R)
+    torch.cuda.synchronize()
+    counts = oracle.expert_counts(idx, E)
+    off = oracle.expert_offsets(counts)
+    pr, rt = oracle.dispatch_slots(idx, E)
+    assert np.array_equal(host(res.expert_counts), counts)
+    assert np.array_equal(host(res.expert_offsets), off)
+    assert np.array_equal(host(res.rank_offsets), oracle.rank_offsets(off, R))
+    assert np.array_equal(host(res.pair_row), pr)
+    assert np.array_equal(host(res.row_token), rt)
+    return res
+
+
+@pytest.mark.parametrize("T,k,E,R", [
+    (1, 1, 1, 1),          # one pair
+    (16, 2, 8, 1),
+    (512, 8, 256, 32),     # P = 4096: largest single-block case
+    (513, 8, 256, 32),     # P = 4104: first multi-block case, ragged last block
+    (3001, 3, 7, 7),       # odd sizes, small E
+    (4096, 8, 1024, 8),    # E = 1024: few blocks with big chunks
+    (20000, 8, 384, 48),
+    (65536, 8, 256, 32),   # many blocks
+])
+def test_send_random_routes(T, k, E, R):
+    rng = np.random.default_rng(T + E)
+    idx = np.argsort(rng.standard_normal((T, E)), axis=1)[:, :k].astype(np.int32)
+    _send_check(idx, E, R)
+
+
+def test_send_all_tokens_one_expert_and_duplicates():
+    # all pairs to one expert (the hottest possible skew), and repeated experts
+    # within a token (dispatch does not need k distinct experts)
+    _send_check(np.full((3000, 4), 5, np.int32), 64, 8)
+    _send_check(np.full((300, 2), 0, np.int32), 8, 1)
+    rng = np.random.default_rng(3)
+    _send_check(rng.integers(0, 16, (5000, 8)).astype(np.int32), 16, 4)
+    _send_check(rng.integers(0, 3, (700, 5)).astype(np.int32), 300, 3)   # mostly empty experts
+
+
+def test_send_drops_out_of_range_experts():
+    m = _m()
+    idx = np.array([[0, 9], [-1, 1], [1, 1]], np.int32)   # 9 and -1 are outside [0, 4)
+    res = m.moe_dispatch_send(dev_i32(idx), 4, 1)
+    torch.cuda.synchronize()
+    assert host(res.expert_counts).tolist() == [1, 3, 0, 0]
+    assert host(res.expert_offsets).tolist() == [0, 1, 4, 4, 4]
+    pr = host(res.pair_row)
+    assert pr.tolist() == [[0, -1], [-1, 1], [2, 3]]
+    assert host(res.row_token)[:4].tolist() == [0, 1, 2, 2]
+
+
+# ------------------------------------------------------------------ recv / combine
+
+@pytest.mark.parametrize("T,H,k", [(1, 8, 1), (3, 8, 2), (37, 296, 3), (1000, 4096, 2),
+                                   (129, 7168, 8), (5, 520, 10), (64, 1024, 32), (300, 64, 4)])
+def test_recv_and_combine_ragged_shapes(T, H, k):
+    m = _m()
+    print(f"[edges] recv/combine T={T} H={H} k={k}", flush=True)
+    rng = np.random.default_rng(T * H + k)
+    P = T * k
+    cap = P + 3
+    pr = rng.permutation(P).reshape(T, k)
+    x = _rand_bf16((T, H), seed=T + 1)
+    buf = torch.full((cap, H), 0x1234, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    m.moe_dispatch_recv(dev_bf16(x), dev_i32(pr), buf=buf)
+    y = _rand_bf16((cap, H), seed=T + 2)
+    w = rng.random((T, k)).astype(np.float32)
+    out = m.moe_combine(dev_bf16(y), dev_i32(pr), dev_f32(w))
+    torch.cuda.synchronize()
+    fill = np.full((cap, H), 0x1234, np.uint16)
+    assert np.array_equal(host_bf16(buf), oracle.dispatch_rows(x, pr, cap, fill))
+    ref = oracle.combine(y, pr, w)
+    assert assert_out_close(host_bf16(out), ref) == 0
+
+
+def test_combine_zero_and_negative_zero_rows():
+    m = _m()
+    T, H, k = 4, 64, 3
+    y = np.zeros((T * k, H), np.uint16)
+    y[1::2] = 0x8000                                 # -0.0 rows
+    pr = np.arange(T * k).reshape(T, k)
+    w = np.full((T, k), 0.5, np.float32)
+    w[0] = -0.5
+    out = host_bf16(m.moe_combine(dev_bf16(y), dev_i32(pr), dev_f32(w)))
+    torch.cuda.synchronize()
+    assert np.array_equal(out, oracle.combine(y, pr, w))
+
+
+def test_combine_rounding_edges():
+    # values around bf16 rounding ties, subnormals, large magnitudes
+    m = _m()
+    T, H, k = 8, 128, 2
+    rng = np.random.default_rng(11)
+    y = rng.integers(0, 2**16, (T * k, H)).astype(np.uint16)
+    exp = (y >> 7) & 0xFF
+    y[exp == 0xFF] &= 0x807F                          # no inf/nan inputs
+    pr = rng.permutation(T * k).reshape(T, k)
+    w = np.array([[1.0, 2.0**-8], [0.5, 0.5], [1.0, 1.0], [1.0, -1.0], [2.0**-30, 2.0**-30],
+                  [3.0, 1.0 / 3.0], [1.0 + 2.0**-8, 1.0], [2.0**40, 2.0**-40]], np.float32)
+    out = m.moe_combine(dev_bf16(y), dev_i32(pr), dev_f32(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16(out), oracle.combine(y, pr, w))
+
+
+# ------------------------------------------------------------------ whole path
+
+def test_identity_experts_round_trip_and_determinism():
+    """route -> dispatch -> combine with y = the dispatch buffer returns x bit
+    for bit, except that -0.0 comes back as +0.0 (the accumulator starts at
+    +0.0); two runs give identical bytes."""
+    m = _m()
+    for name in ["tiny", "mixtral", "dsv3_decode", "kimi_k2"]:
+        wl = workloads.make(name, seed=1, with_y=False)
+        cfg = wl.cfg
+        print(f"[edges] identity round trip {name}", flush=True)
+        x = dev_bf16(wl.x)
+        logits = dev_f32(wl.logits)
+        outs = []
+        for _ in range(2):
+            idx, w = m.moe_route_topk(logits, cfg.k)
+            send, buf = m.moe_dispatch(idx, x, cfg.E, cfg.R)
+            out = m.moe_combine(buf, send.pair_row, w)
+            torch.cuda.synchronize()
+            outs.append((host(idx), host(w), host(send.pair_row), host_bf16(buf), host_bf16(out)))
+        expect = np.where(wl.x == 0x8000, np.uint16(0), wl.x)
+        assert np.array_equal(outs[0][4], expect), name
+        for a, b in zip(outs[0], outs[1]):
+            assert np.array_equal(a, b), name
+
+
+def test_empty_batch_is_a_no_op():
+    m = _m()
+    logits = torch.empty((0, 8), dtype=torch.float32, device=DEV)
+    idx, w = m.moe_route_topk(logits, 2)
+    assert idx.shape == (0, 2)
+    send, buf = m.moe_dispatch(idx, torch.empty((0, 64), dtype=torch.bfloat16, device=DEV), 8, 2)
+    out = m.moe_combine(buf, send.pair_row, w)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64)
+
+
+def test_capacity_errors_raise():
+    m = _m()
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device=DEV)
+    pr = torch.zeros((4, 2), dtype=torch.int32, device=DEV)
+    with pytest.raises(m.MoeError) as ei:
+        m.moe_dispatch_recv(x, pr, buf=torch.zeros((7, 64), dtype=torch.bfloat16, device=DEV))
+    assert ei.value.status == -3

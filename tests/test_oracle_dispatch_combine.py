@@ -133,14 +133,18 @@ def test_combine_exact_on_adversarial_weights():
 def test_identity_experts_return_the_input(name):
     # y = dispatched x with normalised weights: the weighted average of k copies
     # of x[t] is x[t]; fp32 error (< 2^-20 relative) is far below half a bf16
-    # ulp, so the bf16 result is x[t] bit for bit.
+    # ulp, so the bf16 result is x[t] bit for bit, except that -0.0 comes back
+    # as +0.0 because the accumulator starts at +0.0.
     cfg = workloads.CONFIGS[name]
     T = min(cfg.T, 256)
     wl = workloads.make(cfg, T=T, with_y=False)
     idx, _, w32 = oracle.route_topk(wl.logits, cfg.k)
     pr, _ = oracle.dispatch_slots(idx, cfg.E)
-    buf = oracle.dispatch_rows(wl.x, pr, T * cfg.k)
-    assert np.array_equal(oracle.combine(buf, pr, w32), wl.x)
+    x = wl.x.copy()
+    x[:3, :5] = 0x8000                       # plant some -0.0 inputs
+    buf = oracle.dispatch_rows(x, pr, T * cfg.k)
+    expect = np.where(x == 0x8000, np.uint16(0), x)
+    assert np.array_equal(oracle.combine(buf, pr, w32), expect)
 
 
 def test_combine_k1_copies_and_scaling_and_zero():
