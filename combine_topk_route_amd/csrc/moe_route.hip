@@ -8,25 +8,30 @@
 // "Lower latency and higher throughput with multi-node DeepSeek deployment",
 // section "MoE Router".  The pages' kernels target NVSHMEM / EFA on H100 and
 // H200; here everything is one GPU, and the kernels are shaped for wave64,
-// LDS and HBM3E:
+// DPP/ballot cross-lane operations, LDS and HBM3E:
 //
 //   route_topk_kernel    one wave per token: fp32 softmax over E logits held
-//                        in registers, k rounds of a wave-wide arg-max on a
-//                        64-bit (logit, -index) key.
+//                        in registers; k rounds of a wave-wide maximum of an
+//                        order-preserving 32-bit key (DPP row reductions, no
+//                        LDS traffic), the lowest expert index holding it
+//                        found by ballot.
 //   send_hist_kernel     per-block expert histogram; each wave groups equal
-//   send_scan_kernel     experts with ballots so the hot expert costs one LDS
-//   send_rank_kernel     update per wave, not 64.  One block scans the
-//                        [block][expert] counts; the rank kernel gives each
-//                        pair a stable slot (ballot + mbcnt inside a wave,
-//                        LDS prefix across waves, scanned base across blocks).
-//                        Small inputs run all three steps in one block.
-//   dispatch_recv_kernel each token row is read from HBM once with 16-byte
-//                        loads and written to its k rows with 16-byte
-//                        non-temporal stores.
-//   combine_kernel       per token: k independent 16-byte row loads in
-//                        flight, fp32 fma chain in j order, one bf16 RNE
-//                        (v_cvt_pk_bf16_f32), 16-byte stores.  Row indices and
-//                        weights of a token tile are staged in LDS.
+//                        experts with ballots so the hot expert costs one LDS
+//                        update per wave, not 64.
+//   send_rank_kernel     stable slot of every pair: rank among equal experts
+//                        inside a wave (mbcnt), exclusive prefix across waves
+//                        (LDS), and across blocks from the histogram matrix,
+//                        which every block scans for itself.  Small inputs run
+//                        histogram, scan and slots in one block.
+//   dispatch_recv_kernel one block per (token, 1 KiB column slice); each wave
+//                        copies the slice to one of the token's k rows: a
+//                        cached 16-byte load (the block's waves share it) and
+//                        a non-temporal 16-byte store per lane.
+//   combine_kernel       one wave per (token, 1 KiB column slice): k
+//                        non-temporal 16-byte row loads in flight, fp32 fma
+//                        chain in j order, one bf16 RNE (v_cvt_pk_bf16_f32).
+//                        The token's rows and weights come through the scalar
+//                        cache into SGPRs.
 //
 // There is no dense contraction here, so no MFMA: the row kernels are bound by
 // HBM bandwidth and the routing / send kernels by latency.
@@ -65,16 +70,63 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
+// DPP controls (gfx9): quad permutes, row mirrors and the row broadcasts.
+constexpr int kDppQuad1032 = 0xB1;     // quad_perm:[1,0,3,2]
+constexpr int kDppQuad2301 = 0x4E;     // quad_perm:[2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row -> next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 -> rows 2 and 3
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v),
+                                                           CTRL, ROW_MASK, 0xF, false));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+__device__ __forceinline__ uint32_t readlane(uint32_t v, int lane) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), lane));
+}
+
+// Wave-wide reductions over all 64 lanes (all must be active).  The four
+// in-row steps leave every lane of a 16-lane row with the row's result; the
+// two broadcasts fold rows into lane 63, which is read into a scalar.
+__device__ __forceinline__ float wave_max_f32(float v) {
+#define MOE_STEP(CTRL, RM) \
+  v = fmaxf(v, __uint_as_float(dpp<CTRL, RM>(__float_as_uint(v), __float_as_uint(v))))
+  MOE_STEP(kDppQuad1032, 0xF);
+  MOE_STEP(kDppQuad2301, 0xF);
+  MOE_STEP(kDppRowHalfMirror, 0xF);
+  MOE_STEP(kDppRowMirror, 0xF);
+  MOE_STEP(kDppRowBcast15, 0xA);
+  MOE_STEP(kDppRowBcast31, 0xC);
+#undef MOE_STEP
+  return __uint_as_float(readlane(__float_as_uint(v), kWave - 1));
+}
+
+// Fixed association order, so the sum is the same on every run.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#define MOE_STEP(CTRL, RM) v += __uint_as_float(dpp<CTRL, RM>(0u, __float_as_uint(v)))
+  MOE_STEP(kDppQuad1032, 0xF);
+  MOE_STEP(kDppQuad2301, 0xF);
+  MOE_STEP(kDppRowHalfMirror, 0xF);
+  MOE_STEP(kDppRowMirror, 0xF);
+  MOE_STEP(kDppRowBcast15, 0xA);
+  MOE_STEP(kDppRowBcast31, 0xC);
+#undef MOE_STEP
+  return __uint_as_float(readlane(__float_as_uint(v), kWave - 1));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#define MOE_STEP(CTRL, RM) v = max(v, dpp<CTRL, RM>(v, v))
+  MOE_STEP(kDppQuad1032, 0xF);
+  MOE_STEP(kDppQuad2301, 0xF);
+  MOE_STEP(kDppRowHalfMirror, 0xF);
+  MOE_STEP(kDppRowMirror, 0xF);
+  MOE_STEP(kDppRowBcast15, 0xA);
+  MOE_STEP(kDppRowBcast31, 0xC);
+#undef MOE_STEP
+  return readlane(v, kWave - 1);
 }
 
 __device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
@@ -139,7 +191,8 @@ __device__ int32_t block_excl_scan(int32_t* data, int n, int32_t* scratch) {
 // ---------------------------------------------------------------------------
 
 // Monotone map of a float onto uint32 (larger float -> larger key), with -0.0
-// folded into +0.0 so that the two compare equal.
+// folded into +0.0 so that the two compare equal.  Every finite float maps
+// above 0x007FFFFF, so 0 can mark "not a candidate".
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
   u = (u == 0x80000000u) ? 0u : u;
@@ -165,17 +218,19 @@ __global__ __launch_bounds__(kRouteWavesPerBlock* kWave) void route_topk_kernel(
     lv[i] = e < E ? row[e] : -INFINITY;
     m = fmaxf(m, lv[i]);
   }
-  m = wave_max(m);
+  m = wave_max_f32(m);
 
   // Softmax numerators exp(l - m).  The difference is split into its fp32
   // rounding d and the exact remainder r (TwoSum), and exp(d + r) is taken as
   // exp(d) * (1 + r): the subtraction then adds no error of its own.
   float pv[IPL];
+  uint32_t key[IPL];
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < IPL; ++i) {
     const int e = lane + i * kWave;
     float z = 0.f;
+    key[i] = 0u;
     if (e < E) {
       const float a = lv[i], b = -m;
       const float d = a + b;
@@ -183,53 +238,51 @@ __global__ __launch_bounds__(kRouteWavesPerBlock* kWave) void route_topk_kernel(
       const float r = (a - (d - bb)) + (b - bb);
       const float ed = expf(d);
       z = __builtin_fmaf(ed, r, ed);
+      key[i] = order_key(a);
     }
     pv[i] = z;
     s += z;
   }
-  s = wave_sum(s);
+  s = wave_sum_f32(s);
 #pragma unroll
   for (int i = 0; i < IPL; ++i) pv[i] = pv[i] / s;  // fp32 softmax probabilities
 
-  // k rounds of a wave-wide arg-max over the untaken experts.  Key: order_key
-  // of the logit in the high half, ~e in the low half, so equal logits pick
-  // the lower expert index.  Every finite logit has a key above 0.
-  uint32_t taken = 0;
+  // k rounds: the largest remaining key, then the lowest expert index that
+  // holds it (expert e = lane + 64 * i, so the first item slot with a match
+  // and, inside it, the lowest lane).  Selected keys are zeroed.
   int my_e = 0;
   float my_p = 0.f;
   float psum = 0.f, pcomp = 0.f;  // compensated sum of the selected probabilities
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
-    float bestp = 0.f;
+    uint32_t best = 0u;
 #pragma unroll
-    for (int i = 0; i < IPL; ++i) {
-      const int e = lane + i * kWave;
-      if (e < E && !((taken >> i) & 1u)) {
-        const uint64_t key = (uint64_t(order_key(lv[i])) << 32) | uint32_t(~uint32_t(e));
-        if (key > best) {
-          best = key;
-          bestp = pv[i];
-        }
+    for (int i = 0; i < IPL; ++i) best = max(best, key[i]);
+    best = wave_max_u32(best);
+    int item = 0;
+    uint64_t hit = 0;
+#pragma unroll
+    for (int i = IPL - 1; i >= 0; --i) {
+      const uint64_t h = ballot(key[i] == best);
+      if (h != 0) {
+        item = i;
+        hit = h;
       }
     }
+    const int owner = __builtin_ctzll(hit);
+    float cand = pv[0];
 #pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      const uint64_t ob = __shfl_xor(best, off);
-      const float op = __shfl_xor(bestp, off);
-      if (ob > best) {
-        best = ob;
-        bestp = op;
-      }
-    }
-    const uint32_t es = ~uint32_t(best);  // the winning expert, same on every lane
-    if (int(es & (kWave - 1)) == lane) taken |= 1u << (es / kWave);
+    for (int i = 1; i < IPL; ++i) cand = (i == item) ? pv[i] : cand;
+    const float pj = __uint_as_float(readlane(__float_as_uint(cand), owner));
+#pragma unroll
+    for (int i = 0; i < IPL; ++i)
+      if (i == item && lane == owner) key[i] = 0u;
     if (lane == j) {
-      my_e = int(es);
-      my_p = bestp;
+      my_e = item * kWave + owner;
+      my_p = pj;
     }
-    const float ns = psum + bestp;  // TwoSum of the running sum
+    const float ns = psum + pj;  // TwoSum of the running sum
     const float bv = ns - psum;
-    pcomp += (psum - (ns - bv)) + (bestp - bv);
+    pcomp += (psum - (ns - bv)) + (pj - bv);
     psum = ns;
   }
   const float total = psum + pcomp;
@@ -245,10 +298,12 @@ __global__ __launch_bounds__(kRouteWavesPerBlock* kWave) void route_topk_kernel(
 
 constexpr int kSendThreads = 512;
 constexpr int kSendWaves = kSendThreads / kWave;
-constexpr int kScanThreads = 1024;
+constexpr int kSendItems = 4;  // pair indices each lane loads before processing them
 constexpr int64_t kSendFusedMaxPairs = 4096;
 constexpr int64_t kSendChunkTarget = 2048;
-constexpr int kScanLdsCounts = 12288;  // [block][expert] counts staged in the scan block's LDS
+constexpr int kSendMaxBlocks = 64;
+constexpr int kSendMatrixInts = 8192;  // [block][expert] counts staged in LDS by the rank kernel
+constexpr int kLdsInts = 16384;        // 64 KiB of LDS per block at most
 
 struct SendPlan {
   bool fused;
@@ -267,8 +322,10 @@ SendPlan plan_send(int64_t P, int E) {
     return p;
   }
   int64_t nb = (P + kSendChunkTarget - 1) / kSendChunkTarget;
-  int64_t nb_max = kScanLdsCounts / E;
-  if (nb_max > 1024) nb_max = 1024;
+  int64_t nb_max = kSendMatrixInts / E;
+  const int64_t nb_lds = (kLdsInts - (kSendWaves + 1) * E - 17) / E;  // rank kernel's LDS
+  if (nb_max > nb_lds) nb_max = nb_lds;
+  if (nb_max > kSendMaxBlocks) nb_max = kSendMaxBlocks;
   if (nb > nb_max) nb = nb_max;
   if (nb < 1) nb = 1;
   int64_t chunk = (P + nb - 1) / nb;
@@ -302,85 +359,97 @@ __global__ __launch_bounds__(kSendThreads) void send_hist_kernel(const int32_t* 
   __syncthreads();
   int64_t a, b;
   wave_range(P, chunk, a, b);
-  for (int64_t base = a; base < b; base += kWave) {
-    const int64_t p = base + lane_id();
-    int e = p < b ? idx[p] : -1;
-    const bool valid = uint32_t(e) < uint32_t(E);
-    const uint64_t peers = same_expert_lanes(e, valid, nbits);
-    if (valid && lanes_below(peers) == 0) atomicAdd(&hist[e], int32_t(__popcll(peers)));
+  for (int64_t s0 = a; s0 < b; s0 += kWave * kSendItems) {
+    int ev[kSendItems];
+#pragma unroll
+    for (int u = 0; u < kSendItems; ++u) {
+      const int64_t p = s0 + u * kWave + lane_id();
+      ev[u] = p < b ? idx[p] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kSendItems; ++u) {
+      const int e = ev[u];
+      const bool valid = uint32_t(e) < uint32_t(E);
+      const uint64_t peers = same_expert_lanes(e, valid, nbits);
+      if (valid && lanes_below(peers) == 0) atomicAdd(&hist[e], int32_t(__popcll(peers)));
+    }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) ws_cnt[int64_t(blockIdx.x) * E + e] = hist[e];
 }
 
-// One block: for every expert, exclusive scan of the per-block counts (in
-// place, giving each block's first slot inside the expert), then an exclusive
-// scan over experts for the offsets, which is added to the per-block bases.
-__global__ __launch_bounds__(kScanThreads) void send_scan_kernel(
-    int32_t* __restrict__ ws, int nb, int E, int L, int R, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ rank_offsets) {
-  extern __shared__ int32_t sm[];  // [nb*E] counts | [E] totals | [17] scan scratch
-  int32_t* cnt = sm;
-  int32_t* tot = sm + nb * E;
-  int32_t* scratch = tot + E;
-  for (int i = threadIdx.x; i < nb * E; i += blockDim.x) cnt[i] = ws[i];
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int32_t run = 0;
-    for (int b = 0; b < nb; ++b) {
-      const int32_t c = cnt[b * E + e];
-      cnt[b * E + e] = run;
-      run += c;
-    }
-    tot[e] = run;
-    counts[e] = run;
-  }
-  __syncthreads();
-  const int32_t total = block_excl_scan(tot, E, scratch);
-  for (int e = threadIdx.x; e < E; e += blockDim.x) offsets[e] = tot[e];
-  if (threadIdx.x == 0) offsets[E] = total;
-  if (rank_offsets != nullptr) {
-    for (int r = threadIdx.x; r < R; r += blockDim.x) rank_offsets[r] = tot[r * L];
-    if (threadIdx.x == 0) rank_offsets[R] = total;
-  }
-  for (int i = threadIdx.x; i < nb * E; i += blockDim.x) ws[i] = cnt[i] + tot[i % E];
-}
-
 // Stable slot of every pair.  Pass 1: inside each wave, lanes with the same
 // expert are ranked by lane order (mbcnt over the matching-lane mask) on top
 // of the wave's running count kept in LDS; the wave-local slot is parked in
-// pair_row.  Then an exclusive prefix over waves per expert, plus the block's
-// base (multi-block) or the block-wide offsets (fused), completes the row.
+// pair_row.  The expert offsets and this block's first slot in each expert
+// come from the per-block histogram matrix (multi-block) or from the wave
+// counts themselves (FUSED, one block).  Pass 2 adds the exclusive prefix
+// over waves and the block base, and writes row_token.
 template <bool FUSED>
 __global__ __launch_bounds__(kSendThreads) void send_rank_kernel(
-    const int32_t* __restrict__ idx, int64_t P, int E, int k, int nbits, int64_t chunk,
-    const int32_t* __restrict__ ws_base, int L, int R, int32_t* __restrict__ counts,
+    const int32_t* __restrict__ idx, int64_t P, int E, int k, int nbits, int64_t chunk, int nb,
+    const int32_t* __restrict__ ws_cnt, int L, int R, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ rank_offsets,
     int32_t* __restrict__ pair_row, int32_t* __restrict__ row_token) {
-  extern __shared__ int32_t sm[];  // [W][E] per-wave counts | [E] base | [17] scratch
+  // LDS: [W][E] per-wave counts | [E] base | [17] scratch | [nb][E] matrix (multi-block)
+  extern __shared__ int32_t sm[];
   const int nwaves = blockDim.x / kWave;
   const int wid = threadIdx.x / kWave;
   int32_t* hist = sm;
   int32_t* base = sm + nwaves * E;
   int32_t* scratch = base + E;
+  int32_t* mat = scratch + 17;
   for (int i = threadIdx.x; i < nwaves * E; i += blockDim.x) hist[i] = 0;
+  if (!FUSED) {
+    // The [block][expert] histogram matrix (a few KiB, L2-resident), staged
+    // with independent coalesced loads.
+    for (int i = threadIdx.x; i < nb * E; i += blockDim.x) mat[i] = ws_cnt[i];
+  }
   __syncthreads();
+
+  // Multi-block: totals per expert and this block's prefix.  E <= 2 * blockDim.
+  int32_t pre[2] = {0, 0};
+  if (!FUSED) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = threadIdx.x + q * kSendThreads;
+      if (e < E) {
+        int32_t tot = 0, before = 0;
+        for (int b = 0; b < nb; ++b) {
+          const int32_t c = mat[b * E + e];
+          tot += c;
+          before += b < int(blockIdx.x) ? c : 0;
+        }
+        base[e] = tot;
+        pre[q] = before;
+      }
+    }
+  }
 
   int64_t a, b;
   wave_range(P, chunk, a, b);
   int32_t* my_hist = hist + wid * E;
-  for (int64_t s0 = a; s0 < b; s0 += kWave) {
-    const int64_t p = s0 + lane_id();
-    const int e = p < b ? idx[p] : -1;
-    const bool valid = uint32_t(e) < uint32_t(E);
-    const uint64_t peers = same_expert_lanes(e, valid, nbits);
-    if (valid) {
-      const uint32_t below = lanes_below(peers);
-      const int32_t cur = my_hist[e];
-      pair_row[p] = cur + int32_t(below);
-      if (below == 0) my_hist[e] = cur + int32_t(__popcll(peers));
-    } else if (p < b) {
-      pair_row[p] = -1;  // expert index out of range: the pair is dropped
+  for (int64_t s0 = a; s0 < b; s0 += kWave * kSendItems) {
+    int ev[kSendItems];
+#pragma unroll
+    for (int u = 0; u < kSendItems; ++u) {
+      const int64_t p = s0 + u * kWave + lane_id();
+      ev[u] = p < b ? idx[p] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kSendItems; ++u) {
+      const int64_t p = s0 + u * kWave + lane_id();
+      const int e = ev[u];
+      const bool valid = uint32_t(e) < uint32_t(E);
+      const uint64_t peers = same_expert_lanes(e, valid, nbits);
+      if (valid) {
+        const uint32_t below = lanes_below(peers);
+        const int32_t cur = my_hist[e];
+        pair_row[p] = cur + int32_t(below);
+        if (below == 0) my_hist[e] = cur + int32_t(__popcll(peers));
+      } else if (p < b) {
+        pair_row[p] = -1;  // expert index out of range: the pair is dropped
+      }
     }
   }
   __syncthreads();
@@ -392,22 +461,30 @@ __global__ __launch_bounds__(kSendThreads) void send_rank_kernel(
       hist[w * E + e] = run;
       run += c;
     }
-    if (FUSED) {
-      base[e] = run;
-      counts[e] = run;
-    } else {
-      base[e] = ws_base[int64_t(blockIdx.x) * E + e];
-    }
+    if (FUSED) base[e] = run;
   }
   __syncthreads();
-  if (FUSED) {
-    const int32_t total = block_excl_scan(base, E, scratch);
-    for (int e = threadIdx.x; e < E; e += blockDim.x) offsets[e] = base[e];
+  // base[e]: total pairs of expert e -> exclusive offsets.
+  const int32_t total = block_excl_scan(base, E, scratch);
+  if (FUSED || blockIdx.x == 0) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      offsets[e] = base[e];
+      counts[e] = (e + 1 < E ? base[e + 1] : total) - base[e];
+    }
     if (threadIdx.x == 0) offsets[E] = total;
     if (rank_offsets != nullptr) {
       for (int r = threadIdx.x; r < R; r += blockDim.x) rank_offsets[r] = base[r * L];
       if (threadIdx.x == 0) rank_offsets[R] = total;
     }
+  }
+  __syncthreads();
+  if (!FUSED) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = threadIdx.x + q * kSendThreads;
+      if (e < E) base[e] += pre[q];
+    }
+    __syncthreads();
   }
 
   for (int64_t s0 = a; s0 < b; s0 += kWave) {
@@ -424,83 +501,46 @@ __global__ __launch_bounds__(kSendThreads) void send_rank_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dispatch recv and combine: token-tile row kernels
+// dispatch recv and combine: one block per (token, 1 KiB slice of the row)
 // ---------------------------------------------------------------------------
 
-constexpr int kRowThreads = 256;
-constexpr int kRecvUnroll = 4;     // 16-byte row chunks per thread in flight
-constexpr int kCombineUnroll = 1;  // tokens' chunks per thread per step
-constexpr int kCombineGroup = 8;   // expert rows loaded before their fma
+constexpr int kSlice = 64;             // 16-byte chunks per slice: one per lane
+constexpr int kMaxRowThreads = 1024;
+constexpr int64_t kMaxRowBlocks = int64_t(1) << 21;  // beyond this, blocks loop
 
-struct RowPlan {
-  int TT;       // tokens per tile
-  int CW;       // 16-byte chunks per tile (a column slice of the row)
-  int ncs;      // column slices per row
-  int64_t nblocks;
-  size_t lds;
+struct RecvPlan {
+  int groups;  // waves per block; wave g writes destinations g*per .. g*per+per-1
+  int per;
+  int ncs;     // slices per row
+  int64_t units;
+  unsigned nblocks;
 };
 
-RowPlan plan_rows(int64_t T, int C, int k, int unroll, bool with_w, int min_blocks) {
-  RowPlan p{};
-  const int target = kRowThreads * unroll;
-  p.TT = C >= target ? 1 : target / C;
-  p.CW = C;
-  auto blocks = [&](int TT, int CW) {
-    return ((T + TT - 1) / TT) * int64_t((C + CW - 1) / CW);
-  };
-  while (blocks(p.TT, p.CW) < min_blocks) {
-    if (p.TT > 1) {
-      p.TT = (p.TT + 1) / 2;
-    } else if (p.CW > kWave) {
-      p.CW = ((p.CW / 2) + kWave - 1) / kWave * kWave;
-    } else {
-      break;
-    }
-  }
-  p.ncs = (C + p.CW - 1) / p.CW;
-  p.nblocks = blocks(p.TT, p.CW);
-  p.lds = size_t(p.TT) * k * (with_w ? 8 : 4);
+RecvPlan plan_recv(int64_t T, int C, int k) {
+  RecvPlan p{};
+  p.groups = k < kMaxRowThreads / kSlice ? k : kMaxRowThreads / kSlice;
+  p.per = (k + p.groups - 1) / p.groups;
+  p.ncs = (C + kSlice - 1) / kSlice;
+  p.units = T * p.ncs;
+  p.nblocks = unsigned(p.units < kMaxRowBlocks ? p.units : kMaxRowBlocks);
   return p;
 }
 
-__device__ __forceinline__ void tile_coords(int64_t T, int C, int TT, int CW, int ncs, int64_t& t0,
-                                            int& nt, int& c0, int& cw) {
-  const int64_t tile = blockIdx.x / ncs;
-  const int cs = int(blockIdx.x - tile * ncs);
-  t0 = tile * TT;
-  nt = int(T - t0 < TT ? T - t0 : TT);
-  c0 = cs * CW;
-  cw = C - c0 < CW ? C - c0 : CW;
-}
-
-__global__ __launch_bounds__(kRowThreads) void dispatch_recv_kernel(
+__global__ __launch_bounds__(kMaxRowThreads) void dispatch_recv_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ pair_row, int64_t T, int C, int k,
-    int TT, int CW, int ncs, u32x4* __restrict__ buf, int64_t capacity) {
-  extern __shared__ int32_t pr_s[];  // [TT][k]
-  int64_t t0;
-  int nt, c0, cw;
-  tile_coords(T, C, TT, CW, ncs, t0, nt, c0, cw);
-  for (int i = threadIdx.x; i < nt * k; i += blockDim.x) pr_s[i] = pair_row[t0 * k + i];
-  __syncthreads();
-  const int units = nt * cw;
-  for (int ub = 0; ub < units; ub += kRowThreads * kRecvUnroll) {
-    u32x4 v[kRecvUnroll];
-    int tl[kRecvUnroll], c[kRecvUnroll];
-#pragma unroll
-    for (int u = 0; u < kRecvUnroll; ++u) {
-      const int uu = ub + u * kRowThreads + threadIdx.x;
-      tl[u] = nt == 1 ? 0 : uu / cw;
-      c[u] = c0 + uu - tl[u] * cw;
-      if (uu < units) v[u] = __builtin_nontemporal_load(&x[(t0 + tl[u]) * C + c[u]]);
-    }
-#pragma unroll
-    for (int u = 0; u < kRecvUnroll; ++u) {
-      const int uu = ub + u * kRowThreads + threadIdx.x;
-      if (uu < units) {
-        for (int j = 0; j < k; ++j) {
-          const int32_t r = pr_s[tl[u] * k + j];
+    int per, int ncs, int64_t units, u32x4* __restrict__ buf, int64_t capacity) {
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x / kSlice);
+  for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const int64_t t = unit / ncs;
+    const int c = int(unit - t * ncs) * kSlice + lane_id();
+    if (c < C) {
+      const u32x4 v = x[t * C + c];  // cached: the block's waves read the same slice
+      for (int jj = 0; jj < per; ++jj) {
+        const int j = g * per + jj;
+        if (j < k) {
+          const int32_t r = pair_row[t * k + j];
           if (uint64_t(int64_t(r)) < uint64_t(capacity))
-            __builtin_nontemporal_store(v[u], &buf[int64_t(r) * C + c[u]]);
+            __builtin_nontemporal_store(v, &buf[int64_t(r) * C + c]);
         }
       }
     }
@@ -513,63 +553,53 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-__global__ __launch_bounds__(kRowThreads) void combine_kernel(
+constexpr int kCombineGroup = 8;  // expert rows loaded before their fma
+
+__global__ __launch_bounds__(kSlice) void combine_kernel(
     const u32x4* __restrict__ y, const int32_t* __restrict__ pair_row,
-    const float* __restrict__ topk_w, int64_t T, int C, int k, int TT, int CW, int ncs,
+    const float* __restrict__ topk_w, int64_t T, int C, int k, int ncs, int64_t units,
     int64_t capacity, u32x4* __restrict__ out) {
-  extern __shared__ int32_t sm[];  // [TT][k] rows | [TT][k] weights
-  int32_t* pr_s = sm;
-  int64_t t0;
-  int nt, c0, cw;
-  tile_coords(T, C, TT, CW, ncs, t0, nt, c0, cw);
-  float* w_s = reinterpret_cast<float*>(sm + TT * k);
-  for (int i = threadIdx.x; i < nt * k; i += blockDim.x) {
-    pr_s[i] = pair_row[t0 * k + i];
-    w_s[i] = topk_w[t0 * k + i];
-  }
-  __syncthreads();
-  const int units = nt * cw;
-  for (int ub = 0; ub < units; ub += kRowThreads * kCombineUnroll) {
+  for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const int64_t t = unit / ncs;
+    const int c = int(unit - t * ncs) * kSlice + lane_id();
+    if (c >= C) continue;
+    const int32_t* prt = pair_row + t * k;  // uniform: scalar loads into SGPRs
+    const float* wt = topk_w + t * k;
+    float acc[8];
 #pragma unroll
-    for (int u = 0; u < kCombineUnroll; ++u) {
-      const int uu = ub + u * kRowThreads + threadIdx.x;
-      if (uu >= units) continue;
-      const int tl = nt == 1 ? 0 : uu / cw;
-      const int c = c0 + uu - tl * cw;
-      const int32_t* prt = pr_s + tl * k;
-      const float* wt = w_s + tl * k;
-      float acc[8];
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += kCombineGroup) {
+      u32x4 v[kCombineGroup];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-      for (int j0 = 0; j0 < k; j0 += kCombineGroup) {
-        u32x4 v[kCombineGroup];
-#pragma unroll
-        for (int g = 0; g < kCombineGroup; ++g) {
-          v[g] = u32x4{0u, 0u, 0u, 0u};
-          if (j0 + g < k) {
-            const int32_t r = prt[j0 + g];
-            if (uint64_t(int64_t(r)) < uint64_t(capacity))
-              v[g] = __builtin_nontemporal_load(&y[int64_t(r) * C + c]);
-          }
+      for (int g = 0; g < kCombineGroup; ++g) {
+        v[g] = u32x4{0u, 0u, 0u, 0u};
+        if (j0 + g < k) {
+          const int32_t r = prt[j0 + g];
+          if (uint64_t(int64_t(r)) < uint64_t(capacity))
+            v[g] = __builtin_nontemporal_load(&y[int64_t(r) * C + c]);
         }
+      }
 #pragma unroll
-        for (int g = 0; g < kCombineGroup; ++g) {
-          if (j0 + g < k) {
+      for (int g = 0; g < kCombineGroup; ++g) {
+        if (j0 + g < k) {
+          const int32_t r = prt[j0 + g];
+          if (uint64_t(int64_t(r)) < uint64_t(capacity)) {
             const float wj = wt[j0 + g];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const uint32_t word = v[g][q];
               acc[2 * q] = __builtin_fmaf(wj, __uint_as_float(word << 16), acc[2 * q]);
-              acc[2 * q + 1] = __builtin_fmaf(wj, __uint_as_float(word & 0xFFFF0000u), acc[2 * q + 1]);
+              acc[2 * q + 1] =
+                  __builtin_fmaf(wj, __uint_as_float(word & 0xFFFF0000u), acc[2 * q + 1]);
             }
           }
         }
       }
-      u32x4 o;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
-      out[(t0 + tl) * C + c] = o;
     }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    out[t * C + c] = o;
   }
 }
 
@@ -647,34 +677,28 @@ int enqueue_send(const int32_t* topk_idx, int64_t T, int32_t E, int32_t k, int32
   const SendPlan plan = plan_send(P, E);
   const int nbits = nbits_for(E);
   const int L = E / R;
+  const size_t lds = (size_t(kSendWaves) * E + E + 17 + (plan.fused ? 0 : size_t(plan.nb) * E)) *
+                     sizeof(int32_t);
   if (plan.fused) {
-    const size_t lds = (size_t(kSendWaves) * E + E + 17) * sizeof(int32_t);
-    return launch(send_rank_kernel<true>, dim3(1), dim3(kSendThreads), lds, st, topk_idx, P, E,
-                  k, nbits, plan.chunk, static_cast<const int32_t*>(nullptr), L, R, counts,
+    return launch(send_rank_kernel<true>, dim3(1), dim3(kSendThreads), lds, st, topk_idx, P, E, k,
+                  nbits, plan.chunk, 1, static_cast<const int32_t*>(nullptr), L, R, counts,
                   offsets, rank_offsets, pair_row, row_token);
   }
   int32_t* ws = static_cast<int32_t*>(workspace);
-  int rc = launch(send_hist_kernel, dim3(plan.nb), dim3(kSendThreads), size_t(E) * 4, st,
-                  topk_idx, P, E, nbits, plan.chunk, ws);
+  const int rc = launch(send_hist_kernel, dim3(plan.nb), dim3(kSendThreads), size_t(E) * 4, st,
+                        topk_idx, P, E, nbits, plan.chunk, ws);
   if (rc != MOE_OK) return rc;
-  const size_t scan_lds = (size_t(plan.nb) * E + E + 17) * sizeof(int32_t);
-  rc = launch(send_scan_kernel, dim3(1), dim3(kScanThreads), scan_lds, st, ws, plan.nb, E, L, R,
-              counts, offsets, rank_offsets);
-  if (rc != MOE_OK) return rc;
-  const size_t lds = (size_t(kSendWaves) * E + E + 17) * sizeof(int32_t);
   return launch(send_rank_kernel<false>, dim3(plan.nb), dim3(kSendThreads), lds, st, topk_idx, P,
-                E, k, nbits, plan.chunk, static_cast<const int32_t*>(ws), L, R, counts, offsets,
-                rank_offsets, pair_row, row_token);
+                E, k, nbits, plan.chunk, plan.nb, static_cast<const int32_t*>(ws), L, R, counts,
+                offsets, rank_offsets, pair_row, row_token);
 }
-
-int min_row_blocks() { return 1024; }
 
 int enqueue_recv(const void* x, const int32_t* pair_row, int64_t T, int32_t H, int32_t k,
                  void* buf, int64_t capacity, hipStream_t st) {
   const int C = H / 8;
-  const RowPlan p = plan_rows(T, C, k, kRecvUnroll, false, min_row_blocks());
-  return launch(dispatch_recv_kernel, dim3(unsigned(p.nblocks)), dim3(kRowThreads), p.lds, st,
-                static_cast<const u32x4*>(x), pair_row, T, C, k, p.TT, p.CW, p.ncs,
+  const RecvPlan p = plan_recv(T, C, k);
+  return launch(dispatch_recv_kernel, dim3(p.nblocks), dim3(p.groups * kSlice), 0, st,
+                static_cast<const u32x4*>(x), pair_row, T, C, k, p.per, p.ncs, p.units,
                 static_cast<u32x4*>(buf), capacity);
 }
 
@@ -762,10 +786,12 @@ int moe_combine(const void* y, const int32_t* pair_row, const float* topk_w, int
   if (pair_row == nullptr || topk_w == nullptr) return MOE_ERR_INVALID_ARG;
   if (!aligned(pair_row, 4) || !aligned(topk_w, 4)) return MOE_ERR_ALIGNMENT;
   const int C = H / 8;
-  const RowPlan p = plan_rows(T, C, k, 4, true, min_row_blocks());
-  return launch(combine_kernel, dim3(unsigned(p.nblocks)), dim3(kRowThreads), p.lds,
-                static_cast<hipStream_t>(stream), static_cast<const u32x4*>(y), pair_row, topk_w,
-                T, C, k, p.TT, p.CW, p.ncs, capacity, static_cast<u32x4*>(out));
+  const int ncs = (C + kSlice - 1) / kSlice;
+  const int64_t units = T * ncs;
+  const unsigned nblocks = unsigned(units < kMaxRowBlocks ? units : kMaxRowBlocks);
+  return launch(combine_kernel, dim3(nblocks), dim3(kSlice), 0, static_cast<hipStream_t>(stream),
+                static_cast<const u32x4*>(y), pair_row, topk_w, T, C, k, ncs, units, capacity,
+                static_cast<u32x4*>(out));
 }
 
 }  // extern "C"
