@@ -94,6 +94,7 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -131,23 +132,24 @@ def main() -> int:
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step(ev=None, st=None):
+        st = stream if st is None else st
         if ev is not None:
-            ev[0].record(stream)
-        m.moe_route_topk(logits, k, topk_idx=idx, topk_w=w, stream=stream)
+            ev[0].record(st)
+        m.moe_route_topk(logits, k, topk_idx=idx, topk_w=w, stream=st)
         if ev is not None:
-            ev[1].record(stream)
+            ev[1].record(st)
         m.moe_dispatch_send(idx, E, R, expert_counts=counts, expert_offsets=offsets,
                             pair_row=pair_row, row_token=row_token, rank_offsets=rank_off,
-                            workspace=ws, stream=stream)
+                            workspace=ws, stream=st)
         if ev is not None:
-            ev[2].record(stream)
-        m.moe_dispatch_recv(x, pair_row, buf=buf, stream=stream)
+            ev[2].record(st)
+        m.moe_dispatch_recv(x, pair_row, buf=buf, stream=st)
         if ev is not None:
-            ev[3].record(stream)
-        m.moe_combine(y, pair_row, w, out=out, stream=stream)
+            ev[3].record(st)
+        m.moe_combine(y, pair_row, w, out=out, stream=st)
         if ev is not None:
-            ev[4].record(stream)
+            ev[4].record(st)
 
     for _ in range(args.warmup):
         step()
@@ -175,6 +177,31 @@ def main() -> int:
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
+
+    # Timed region 3: the step captured once into a HIP graph (no host-side
+    # knowledge of routed counts is needed, so one graph serves any routing)
+    # and replayed K times.
+    graph_ms = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(st=side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step(st=torch.cuda.current_stream())
+        g.replay()
+        torch.cuda.synchronize()
+        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ga.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        gb.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = ga.elapsed_time(gb) / args.steps
+        del g
 
     names = ["route", "dispatch_send", "dispatch_recv", "combine"]
     per = {n: [] for n in names}
@@ -241,6 +268,9 @@ def main() -> int:
             "traffic": traffic,
         },
         "kernels": kernels,
+        "graph_replay": None if graph_ms is None else {
+            "ms_per_step": round(graph_ms, 4),
+            "tokens_per_s": round(T / (graph_ms * 1e-3), 1)},
         "copy_1GiB_GBps": None if copy_gbps is None else round(copy_gbps, 1),
         "host_wall_s": round(t_host, 3),
     }

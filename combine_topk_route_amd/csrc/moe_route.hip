@@ -402,8 +402,22 @@ __global__ __launch_bounds__(kSendThreads) void send_rank_kernel(
   for (int i = threadIdx.x; i < nwaves * E; i += blockDim.x) hist[i] = 0;
   if (!FUSED) {
     // The [block][expert] histogram matrix (a few KiB, L2-resident), staged
-    // with independent coalesced loads.
-    for (int i = threadIdx.x; i < nb * E; i += blockDim.x) mat[i] = ws_cnt[i];
+    // with batches of independent coalesced loads.
+    constexpr int kBatch = 16;
+    const int n = nb * E;
+    for (int i0 = threadIdx.x; i0 < n; i0 += kSendThreads * kBatch) {
+      int32_t v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int i = i0 + u * kSendThreads;
+        v[u] = i < n ? ws_cnt[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int i = i0 + u * kSendThreads;
+        if (i < n) mat[i] = v[u];
+      }
+    }
   }
   __syncthreads();
 
@@ -429,6 +443,11 @@ __global__ __launch_bounds__(kSendThreads) void send_rank_kernel(
   int64_t a, b;
   wave_range(P, chunk, a, b);
   int32_t* my_hist = hist + wid * E;
+  // A wave whose range fits in one step keeps experts and local slots in
+  // registers for pass 2; longer ranges park the local slot in pair_row.
+  const bool one_step = b - a <= int64_t(kWave) * kSendItems;
+  int keep_e[kSendItems];
+  int32_t keep_slot[kSendItems];
   for (int64_t s0 = a; s0 < b; s0 += kWave * kSendItems) {
     int ev[kSendItems];
 #pragma unroll
@@ -442,14 +461,16 @@ __global__ __launch_bounds__(kSendThreads) void send_rank_kernel(
       const int e = ev[u];
       const bool valid = uint32_t(e) < uint32_t(E);
       const uint64_t peers = same_expert_lanes(e, valid, nbits);
+      int32_t slot = -1;  // -1: expert index out of range, the pair is dropped
       if (valid) {
         const uint32_t below = lanes_below(peers);
         const int32_t cur = my_hist[e];
-        pair_row[p] = cur + int32_t(below);
+        slot = cur + int32_t(below);
         if (below == 0) my_hist[e] = cur + int32_t(__popcll(peers));
-      } else if (p < b) {
-        pair_row[p] = -1;  // expert index out of range: the pair is dropped
       }
+      keep_e[u] = e;
+      keep_slot[u] = slot;
+      if (!one_step && p < b) pair_row[p] = slot;
     }
   }
   __syncthreads();
@@ -487,14 +508,26 @@ __global__ __launch_bounds__(kSendThreads) void send_rank_kernel(
     __syncthreads();
   }
 
-  for (int64_t s0 = a; s0 < b; s0 += kWave) {
-    const int64_t p = s0 + lane_id();
-    if (p < b) {
-      const int e = idx[p];
-      if (uint32_t(e) < uint32_t(E)) {
-        const int32_t r = base[e] + my_hist[e] + pair_row[p];
+  for (int64_t s0 = a; s0 < b; s0 += kWave * kSendItems) {
+    if (!one_step) {
+#pragma unroll
+      for (int u = 0; u < kSendItems; ++u) {
+        const int64_t p = s0 + u * kWave + lane_id();
+        keep_e[u] = p < b ? idx[p] : -1;
+        keep_slot[u] = p < b ? pair_row[p] : -1;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kSendItems; ++u) {
+      const int64_t p = s0 + u * kWave + lane_id();
+      if (p < b) {
+        const int e = keep_e[u];
+        int32_t r = -1;
+        if (uint32_t(e) < uint32_t(E)) {
+          r = base[e] + my_hist[e] + keep_slot[u];
+          row_token[r] = int32_t(p) / k;
+        }
         pair_row[p] = r;
-        row_token[r] = int32_t(p) / k;
       }
     }
   }
