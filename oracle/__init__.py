@@ -24,3 +24,11 @@ from .moe import (  # noqa: F401
     combine_exact,
     fmaf_exact,
 )
+from .quant import (  # noqa: F401
+    E4M3_MAX,
+    e4m3_decode,
+    e4m3_encode,
+    quantize_rows,
+    dequantize_rows,
+    dispatch_rows_fp8,
+)
