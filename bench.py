@@ -203,6 +203,29 @@ def main() -> int:
         graph_ms = ga.elapsed_time(gb) / args.steps
         del g
 
+    # Block-scaled fp8 dispatch recv (same routing; codes + fp32 scales per
+    # 128 elements), timed on its own with an event pair per launch.
+    fp8 = None
+    if H % 128 == 0:
+        buf_q = torch.empty((P, H), dtype=torch.uint8, device=dev)
+        buf_s = torch.empty((P, H // 128), dtype=torch.float32, device=dev)
+        m.moe_dispatch_recv_fp8(x, pair_row, buf_q=buf_q, buf_scale=buf_s, stream=stream)
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a_, b_ in fev:
+            a_.record(stream)
+            m.moe_dispatch_recv_fp8(x, pair_row, buf_q=buf_q, buf_scale=buf_s, stream=stream)
+            b_.record(stream)
+        torch.cuda.synchronize()
+        us = 1000.0 * float(np.mean([a_.elapsed_time(b_) for a_, b_ in fev]))
+        fb = 2 * T * H + P * H + 4 * P * (H // 128) + 4 * P
+        fp8 = {"us_mean": round(us, 2), "bytes": fb, "GBps": round(fb / (us * 1e-6) / 1e9, 1),
+               "frac_of_peak": round(fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+               "traffic": measured_traffic("fp8_dispatch_recv"),
+               "speedup_vs_bf16_recv": None}
+        del buf_q, buf_s
+
     names = ["route", "dispatch_send", "dispatch_recv", "combine"]
     per = {n: [] for n in names}
     for e in evs:
@@ -218,6 +241,8 @@ def main() -> int:
                       "bytes": nbytes[n], "GBps": round(gbps, 1),
                       "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
     dom = max(["dispatch_recv", "combine"], key=lambda n: kernels[n]["us_mean"])
+    if fp8 is not None:
+        fp8["speedup_vs_bf16_recv"] = round(kernels["dispatch_recv"]["us_mean"] / fp8["us_mean"], 3)
     step_bytes = sum(nbytes.values())
     tokens_per_s = T * args.steps / (total_ms * 1e-3)
 
@@ -268,6 +293,7 @@ def main() -> int:
             "traffic": traffic,
         },
         "kernels": kernels,
+        "fp8_dispatch_recv": fp8,
         "graph_replay": None if graph_ms is None else {
             "ms_per_step": round(graph_ms, 4),
             "tokens_per_s": round(T / (graph_ms * 1e-3), 1)},

@@ -11,6 +11,8 @@ from .binding import (  # noqa: F401
     moe_abi_version,
     moe_combine,
     moe_dispatch,
+    moe_dispatch_fp8,
+    moe_dispatch_recv_fp8,
     moe_dispatch_recv,
     moe_dispatch_send,
     moe_dispatch_workspace_bytes,

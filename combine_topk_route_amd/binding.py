@@ -189,6 +189,66 @@ def moe_dispatch(topk_idx: torch.Tensor, x: torch.Tensor, E: int, num_vranks: in
     return out, buf
 
 
+def _fp8_bufs(x, T, k, buf_q, buf_scale, capacity):
+    H = x.shape[1]
+    rows = T * k if capacity is None else capacity
+    if buf_q is None:
+        buf_q = _empty((rows, H), torch.uint8, x)
+    if buf_scale is None:
+        buf_scale = _empty((rows, H // 128 if H % 128 == 0 else 0), torch.float32, x)
+    if capacity is None:
+        capacity = buf_q.shape[0]
+    if buf_q.dim() != 2 or buf_q.shape[1] != H or buf_q.shape[0] < capacity:
+        raise ValueError("buf_q must be [>= capacity, H] uint8")
+    if buf_scale.dim() != 2 or buf_scale.shape[0] < capacity or buf_scale.shape[1] != H // 128:
+        raise ValueError("buf_scale must be [>= capacity, H // 128] float32")
+    return buf_q, buf_scale, capacity
+
+
+def moe_dispatch_recv_fp8(x: torch.Tensor, pair_row: torch.Tensor, buf_q=None, buf_scale=None,
+                          capacity: Optional[int] = None, stream=None):
+    """Scatter block-scaled fp8 (E4M3) token rows: returns (buf_q uint8
+    [capacity, H], buf_scale fp32 [capacity, H/128])."""
+    xp = _dev(x, "x", torch.bfloat16, 2)
+    T, H = x.shape
+    if pair_row.dim() != 2 or pair_row.shape[0] != T:
+        raise ValueError("pair_row must be [T, k]")
+    k = pair_row.shape[1]
+    buf_q, buf_scale, capacity = _fp8_bufs(x, T, k, buf_q, buf_scale, capacity)
+    _check("moe_dispatch_recv_fp8", _lib.load().moe_dispatch_recv_fp8(
+        xp, _dev(pair_row, "pair_row", torch.int32), T, H, k,
+        _dev(buf_q, "buf_q", torch.uint8), _dev(buf_scale, "buf_scale", torch.float32),
+        capacity, _stream(stream)))
+    return buf_q, buf_scale
+
+
+def moe_dispatch_fp8(topk_idx: torch.Tensor, x: torch.Tensor, E: int, num_vranks: int = 1, *,
+                     buf_q=None, buf_scale=None, capacity=None, expert_counts=None,
+                     expert_offsets=None, pair_row=None, row_token=None, rank_offsets=None,
+                     with_rank_offsets: bool = True, workspace=None, stream=None):
+    """Send then fp8 receive on one stream; returns (SendResult, buf_q, buf_scale)."""
+    ip = _dev(topk_idx, "topk_idx", torch.int32, 2)
+    xp = _dev(x, "x", torch.bfloat16, 2)
+    T, k = topk_idx.shape
+    H = x.shape[1]
+    if x.shape[0] != T:
+        raise ValueError("x and topk_idx disagree on T")
+    out = _send_outputs(topk_idx, E, num_vranks, expert_counts, expert_offsets, pair_row,
+                        row_token, rank_offsets, with_rank_offsets)
+    buf_q, buf_scale, capacity = _fp8_bufs(x, T, k, buf_q, buf_scale, capacity)
+    wp, wn, _ = _workspace(T, E, k, workspace, topk_idx)
+    rp = _dev(out.rank_offsets, "rank_offsets", torch.int32) if out.rank_offsets is not None else None
+    _check("moe_dispatch_fp8", _lib.load().moe_dispatch_fp8(
+        ip, xp, T, E, k, H, num_vranks,
+        _dev(out.expert_counts, "expert_counts", torch.int32),
+        _dev(out.expert_offsets, "expert_offsets", torch.int32),
+        _dev(out.pair_row, "pair_row", torch.int32),
+        _dev(out.row_token, "row_token", torch.int32), rp,
+        _dev(buf_q, "buf_q", torch.uint8), _dev(buf_scale, "buf_scale", torch.float32),
+        capacity, wp, wn, _stream(stream)))
+    return out, buf_q, buf_scale
+
+
 def moe_combine(y: torch.Tensor, pair_row: torch.Tensor, topk_w: torch.Tensor,
                 out: Optional[torch.Tensor] = None, capacity: Optional[int] = None,
                 stream=None) -> torch.Tensor:

@@ -27,6 +27,12 @@
 //                        copies the slice to one of the token's k rows: a
 //                        cached 16-byte load (the block's waves share it) and
 //                        a non-temporal 16-byte store per lane.
+//   dispatch_recv_fp8_kernel
+//                        the same scatter with block-scaled fp8 payloads:
+//                        each 16-lane DPP row holds one 128-element block, so
+//                        its amax is an in-row DPP maximum; the block's waves
+//                        quantise 8 slices into LDS once, then each wave
+//                        streams one destination row's codes and scales.
 //   combine_kernel       one wave per (token, 1 KiB column slice): k
 //                        non-temporal 16-byte row loads in flight, fp32 fma
 //                        chain in j order, one bf16 RNE (v_cvt_pk_bf16_f32).
@@ -580,6 +586,100 @@ __global__ __launch_bounds__(kMaxRowThreads) void dispatch_recv_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp8 dispatch recv: block-scaled OCP E4M3 payloads
+// ---------------------------------------------------------------------------
+
+constexpr int kQuantBlock = 128;         // elements per scale
+constexpr float kE4M3Max = 448.0f;       // largest finite E4M3 value
+constexpr int kFp8Waves = 8;             // slices quantised per block
+constexpr int kFp8SliceElems = kSlice * 8;
+constexpr int kFp8BlockElems = kFp8Waves * kFp8SliceElems;  // 4096 elements per block
+
+// Nearest E4M3 (4 exponent bits, bias 7, 3 mantissa bits, no infinities)
+// code of a finite fp32, ties to the even code, saturating at +-448.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x43E00000u) {         // |v| >= 448: saturate (NaN stays NaN)
+    code = a > 0x7F800000u ? 0x7Fu : 0x7Eu;
+  } else if (a >= 0x3C800000u) {  // |v| >= 2^-6: normal; round the mantissa at bit 20
+    code = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+  } else {                        // subnormal E4M3: multiples of 2^-9 (scaling is exact)
+    code = uint32_t(__builtin_rintf(__uint_as_float(a) * 512.0f));
+  }
+  return sign | code;
+}
+
+// Maximum over the 16 lanes of each DPP row (every lane gets its row's value).
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = max(v, dpp<kDppQuad1032, 0xF>(v, v));
+  v = max(v, dpp<kDppQuad2301, 0xF>(v, v));
+  v = max(v, dpp<kDppRowHalfMirror, 0xF>(v, v));
+  v = max(v, dpp<kDppRowMirror, 0xF>(v, v));
+  return v;
+}
+
+__global__ __launch_bounds__(kFp8Waves* kWave) void dispatch_recv_fp8_kernel(
+    const u32x4* __restrict__ x, const int32_t* __restrict__ pair_row, int64_t T, int C, int H,
+    int k, int nsb, int64_t units, uint8_t* __restrict__ buf_q, float* __restrict__ buf_s,
+    int64_t capacity) {
+  __shared__ u32x4 q_lds[kFp8BlockElems / 16];         // 4 KiB of codes
+  __shared__ float s_lds[kFp8BlockElems / kQuantBlock];  // 32 scales
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = lane_id();
+  const int nscale = H / kQuantBlock;
+  for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const int64_t t = unit / nsb;
+    const int sb = int(unit - t * nsb);
+    // Phase 1: wave w quantises slice sb*8 + w (512 elements, 4 scale blocks).
+    const int c = (sb * kFp8Waves + w) * kSlice + lane;  // 16-byte chunk of the bf16 row
+    const bool live = c < C;  // whole 16-lane rows are live or not (H % 128 == 0)
+    const u32x4 v = live ? x[t * C + c] : u32x4{0u, 0u, 0u, 0u};
+    float f[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f[2 * q] = __uint_as_float(v[q] << 16);
+      f[2 * q + 1] = __uint_as_float(v[q] & 0xFFFF0000u);
+    }
+    uint32_t amax_bits = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax_bits = max(amax_bits, __float_as_uint(f[i]) & 0x7FFFFFFFu);
+    amax_bits = row16_max_u32(amax_bits);
+    const float amax = __uint_as_float(amax_bits);
+    const float scale = amax > 0.f ? amax / kE4M3Max : 1.0f;
+    uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= e4m3_code(f[i] / scale) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= e4m3_code(f[4 + i] / scale) << (8 * i);
+    reinterpret_cast<uint2*>(q_lds)[w * kWave + lane] = make_uint2(lo, hi);
+    if ((lane & 15) == 0) s_lds[w * 4 + lane / 16] = scale;
+    __syncthreads();
+    // Phase 2: wave w writes the block's codes and scales to destinations
+    // w, w + 8, ... of token t.
+    const int e0 = sb * kFp8BlockElems;
+    const int nbytes = H - e0 < kFp8BlockElems ? H - e0 : kFp8BlockElems;
+    const int nunits = nbytes / 16;
+    const int ns = nbytes / kQuantBlock;
+    for (int j = w; j < k; j += kFp8Waves) {
+      const int32_t r = pair_row[t * k + j];
+      if (uint64_t(int64_t(r)) < uint64_t(capacity)) {
+        u32x4* dq = reinterpret_cast<u32x4*>(buf_q + int64_t(r) * H + e0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int unit16 = u * kWave + lane;
+          if (unit16 < nunits) __builtin_nontemporal_store(q_lds[unit16], &dq[unit16]);
+        }
+        if (lane < ns) buf_s[int64_t(r) * nscale + e0 / kQuantBlock + lane] = s_lds[lane];
+      }
+    }
+    __syncthreads();  // the LDS tiles are reused by the next unit
+  }
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2 f = {lo, hi};
   const bf16x2 h = __builtin_convertvector(f, bf16x2);  // round-to-nearest-even
@@ -735,6 +835,28 @@ int enqueue_recv(const void* x, const int32_t* pair_row, int64_t T, int32_t H, i
                 static_cast<u32x4*>(buf), capacity);
 }
 
+int check_fp8_rows(int64_t T, int32_t H, int32_t k, int64_t capacity, const void* x,
+                   const void* buf_q, const void* buf_s) {
+  const int st = check_rows(T, H, k, capacity, x, buf_q);
+  if (st != MOE_OK) return st;
+  if (H % kQuantBlock != 0) return MOE_ERR_ALIGNMENT;
+  if (T == 0) return MOE_OK;
+  if (buf_s == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(buf_s, 4)) return MOE_ERR_ALIGNMENT;
+  return MOE_OK;
+}
+
+int enqueue_recv_fp8(const void* x, const int32_t* pair_row, int64_t T, int32_t H, int32_t k,
+                     void* buf_q, float* buf_s, int64_t capacity, hipStream_t st) {
+  const int C = H / 8;
+  const int nsb = (H + kFp8BlockElems - 1) / kFp8BlockElems;
+  const int64_t units = T * nsb;
+  const unsigned nblocks = unsigned(units < kMaxRowBlocks ? units : kMaxRowBlocks);
+  return launch(dispatch_recv_fp8_kernel, dim3(nblocks), dim3(kFp8Waves * kWave), 0, st,
+                static_cast<const u32x4*>(x), pair_row, T, C, H, k, nsb, units,
+                static_cast<uint8_t*>(buf_q), buf_s, capacity);
+}
+
 }  // namespace
 
 extern "C" {
@@ -810,6 +932,33 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int64_t T, int32_t E, i
                     row_token, rank_offsets, workspace, s);
   if (st != MOE_OK) return st;
   return enqueue_recv(x, pair_row, T, H, k, buf, capacity, s);
+}
+
+int moe_dispatch_recv_fp8(const void* x, const int32_t* pair_row, int64_t T, int32_t H, int32_t k,
+                          void* buf_q, float* buf_scale, int64_t capacity, void* stream) {
+  const int st = check_fp8_rows(T, H, k, capacity, x, buf_q, buf_scale);
+  if (st != MOE_OK || T == 0) return st;
+  if (pair_row == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(pair_row, 4)) return MOE_ERR_ALIGNMENT;
+  return enqueue_recv_fp8(x, pair_row, T, H, k, buf_q, buf_scale, capacity,
+                          static_cast<hipStream_t>(stream));
+}
+
+int moe_dispatch_fp8(const int32_t* topk_idx, const void* x, int64_t T, int32_t E, int32_t k,
+                     int32_t H, int32_t num_vranks, int32_t* expert_counts,
+                     int32_t* expert_offsets, int32_t* pair_row, int32_t* row_token,
+                     int32_t* rank_offsets, void* buf_q, float* buf_scale, int64_t capacity,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_send(topk_idx, T, E, k, num_vranks, expert_counts, expert_offsets, pair_row,
+                      row_token, rank_offsets, workspace, workspace_bytes);
+  if (st != MOE_OK) return st;
+  st = check_fp8_rows(T, H, k, capacity, x, buf_q, buf_scale);
+  if (st != MOE_OK || T == 0) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = enqueue_send(topk_idx, T, E, k, num_vranks, expert_counts, expert_offsets, pair_row,
+                    row_token, rank_offsets, workspace, s);
+  if (st != MOE_OK) return st;
+  return enqueue_recv_fp8(x, pair_row, T, H, k, buf_q, buf_scale, capacity, s);
 }
 
 int moe_combine(const void* y, const int32_t* pair_row, const float* topk_w, int64_t T, int32_t H,

@@ -168,6 +168,43 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int64_t T, int32_t E,
                  size_t workspace_bytes, void* stream);
 
 /*
+ * moe_dispatch_recv_fp8 - moe_dispatch_recv with block-scaled fp8 payloads:
+ * each token row is quantised on the fly with one scale per 128-element block
+ * and the fp8 row plus its scales are written to the token's k rows
+ * ("Lower latency and higher throughput with multi-node DeepSeek
+ * deployment", section "Quantization"; "Efficient and portable
+ * mixture-of-experts communication", section "Dispatch": tokens travel with
+ * their block scale factors; combine stays 16-bit).
+ *
+ *   x         [T, H] bf16 (16-byte aligned), H % 128 == 0, finite values.
+ *   pair_row  [T, k] int32: as for moe_dispatch_recv (out-of-range skipped).
+ *   buf_q     [capacity, H] uint8 (out, 16-byte aligned): OCP E4M3 codes
+ *             (4 exponent bits, bias 7, 3 mantissa bits, no infinities).
+ *   buf_scale [capacity, H/128] fp32 (out, 4-byte aligned).
+ * For block b of token t: amax = max |x[t, 128b : 128b+128]|;
+ * scale = amax / 448 in fp32 (1.0 when amax == 0); every code is the nearest
+ * E4M3 value to fp32(x / scale), ties to the even code, saturating at +-448.
+ * Dequantised value = E4M3(code) * scale.
+ * Errors: as moe_dispatch_recv, plus MOE_ERR_ALIGNMENT when H % 128 != 0,
+ *         MOE_ERR_INVALID_ARG for a NULL buf_scale.
+ */
+int moe_dispatch_recv_fp8(const void* x, const int32_t* pair_row, int64_t T,
+                          int32_t H, int32_t k, void* buf_q, float* buf_scale,
+                          int64_t capacity, void* stream);
+
+/*
+ * moe_dispatch_fp8 - moe_dispatch_send followed by moe_dispatch_recv_fp8 on
+ * one stream; arguments as theirs, all checked before anything is enqueued.
+ */
+int moe_dispatch_fp8(const int32_t* topk_idx, const void* x, int64_t T,
+                     int32_t E, int32_t k, int32_t H, int32_t num_vranks,
+                     int32_t* expert_counts, int32_t* expert_offsets,
+                     int32_t* pair_row, int32_t* row_token,
+                     int32_t* rank_offsets, void* buf_q, float* buf_scale,
+                     int64_t capacity, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
  * moe_combine - receiver-side weighted sum of each token's k expert-output
  * rows ("Efficient and portable mixture-of-experts communication", section
  * "Combine"; accumulation at the receiver as in "Enabling trillion-parameter

@@ -159,3 +159,27 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def test_fp8_dispatch_rejects_bad_arguments(lib):
+    r = lib.moe_dispatch_recv_fp8
+    assert r(P16, P16, 16, 256, 2, P16, P16, 31, S) == CAP
+    assert r(P16, P16, 16, 264, 2, P16, P16, 32, S) == ALIGN      # H % 128 != 0 (but % 8 == 0)
+    assert r(P16, P16, 16, 256, 2, P4, P16, 32, S) == ALIGN       # codes not 16-byte aligned
+    assert r(P16, P16, 16, 256, 2, P16, P16 + 2, 32, S) == ALIGN  # scales not 4-byte aligned
+    assert r(P16, P16, 16, 256, 2, P16, None, 32, S) == INVALID
+    assert r(P16, None, 16, 256, 2, P16, P16, 32, S) == INVALID
+    assert r(None, None, 0, 256, 2, None, None, 0, S) == OK
+    f = lib.moe_dispatch_fp8
+    ws = lib.moe_dispatch_workspace_bytes(8192, 256, 8)
+    base = [P16, P16, 8192, 256, 8, 7168, 32, P16, P16, P16, P16, None, P16, P16, 8192 * 8, P16,
+            ws, S]
+    bad = list(base)
+    bad[5] = 7176                    # H % 128 != 0
+    assert f(*bad) == ALIGN
+    bad = list(base)
+    bad[13] = None                   # no scale buffer
+    assert f(*bad) == INVALID
+    bad = list(base)
+    bad[6] = 7                       # E % R != 0
+    assert f(*bad) == INVALID

@@ -1,0 +1,88 @@
+"""GPU parity for block-scaled fp8 dispatch: E4M3 codes and fp32 scales must
+be bit-exact with the oracle (the division x/scale and the rounding to E4M3
+are taken in fp32 on both sides)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpuhelp import DEV, dev_bf16, dev_i32, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _fp8_check(x_bits, pr, cap=None, label=""):
+    import combine_topk_route_amd as m
+
+    T, H = x_bits.shape
+    k = pr.shape[1]
+    cap = T * k + 3 if cap is None else cap
+    print(f"[fp8] {label} T={T} H={H} k={k} capacity={cap}", flush=True)
+    bq = torch.full((cap, H), 0x5A, dtype=torch.uint8, device=DEV)
+    bs = torch.full((cap, H // 128), -2.0, dtype=torch.float32, device=DEV)
+    m.moe_dispatch_recv_fp8(dev_bf16(x_bits), dev_i32(pr), buf_q=bq, buf_scale=bs)
+    torch.cuda.synchronize()
+    rq, rs = oracle.dispatch_rows_fp8(x_bits, pr, cap, np.full((cap, H), 0x5A, np.uint8),
+                                      np.full((cap, H // 128), -2.0, np.float32))
+    gq, gs = host(bq), host(bs)
+    assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32)), "scales differ"
+    bad = np.argwhere(gq != rq)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("name", list(workloads.CONFIGS))
+def test_fp8_dispatch_parity_on_configs(name):
+    wl = workloads.make(name, seed=0, with_y=False)
+    cfg = wl.cfg
+    idx, _, _ = oracle.route_topk(wl.logits, cfg.k)
+    pr, _ = oracle.dispatch_slots(idx, cfg.E)
+    _fp8_check(wl.x, pr, label=name)
+
+
+@pytest.mark.parametrize("T,H,k", [(1, 128, 1), (3, 384, 3), (37, 640, 10), (64, 1024, 32),
+                                   (129, 7168, 8), (5, 4224, 2), (300, 128, 4)])
+def test_fp8_dispatch_ragged_shapes(T, H, k):
+    rng = np.random.default_rng(T * H + k)
+    x = workloads.bf16_from_f32(rng.standard_normal((T, H)).astype(np.float32))
+    pr = rng.permutation(T * k).reshape(T, k)
+    _fp8_check(x, pr, label="ragged")
+
+
+def test_fp8_special_values():
+    rng = np.random.default_rng(77)
+    T, H = 8, 1024
+    f = rng.standard_normal((T, H)).astype(np.float32)
+    f[0, :128] = 0.0                                   # zero block -> scale 1, codes 0
+    f[0, 128:256] = -0.0                               # -0 block -> codes 0x80
+    f[1, :128] = rng.standard_normal(128) * 1e30       # huge magnitudes
+    f[1, 128:256] = rng.standard_normal(128) * 1e-30   # tiny magnitudes
+    f[2, :128] = 1e-38 * rng.standard_normal(128)      # bf16 subnormals
+    f[3, :128] = 1.0
+    f[3, 1:64] = 1.0625                                # x/scale = 1.0625*448/amax: E4M3 ties
+    f[3, 0] = 448.0                                    # amax 448 -> scale exactly 1
+    f[4, :128] = np.where(np.arange(128) % 2, 3e4, -1e-3)  # wide range inside one block
+    f[5] = np.linspace(-7, 7, H)
+    x = workloads.bf16_from_f32(f)
+    x[6, :128] = 0x0001                                # smallest positive bf16 subnormal
+    x[7, :128] = 0x7F7F                                # largest finite bf16
+    pr = np.arange(T).reshape(T, 1)
+    _fp8_check(x, pr, label="special")
+
+
+def test_fp8_chain_matches_oracle():
+    import combine_topk_route_amd as m
+
+    wl = workloads.make("kimi_k2", seed=2, with_y=False)
+    cfg = wl.cfg
+    print("[fp8] chain kimi_k2 route -> moe_dispatch_fp8", flush=True)
+    from gpuhelp import dev_f32
+    idx, w = m.moe_route_topk(dev_f32(wl.logits), cfg.k)
+    send, bq, bs = m.moe_dispatch_fp8(idx, dev_bf16(wl.x), cfg.E, cfg.R)
+    torch.cuda.synchronize()
+    r_idx, _, _ = oracle.route_topk(wl.logits, cfg.k)
+    pr, rt = oracle.dispatch_slots(r_idx, cfg.E)
+    assert np.array_equal(host(send.pair_row), pr)
+    rq, rs = oracle.dispatch_rows_fp8(wl.x, pr, cfg.P)
+    assert np.array_equal(host(bs).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(host(bq), rq)
