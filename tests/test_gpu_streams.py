@@ -1,0 +1,63 @@
+"""Send, recv and combine on different HIP streams joined by events (the
+send/recv split exists so other work can run between them), and the
+block-loop path of the row kernels (more row units than one launch holds)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpuhelp import DEV, assert_out_close, dev_bf16, dev_f32, dev_i32, host, host_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def test_send_recv_combine_on_separate_streams():
+    import combine_topk_route_amd as m
+
+    wl = workloads.make("mixtral", seed=5)
+    cfg = wl.cfg
+    print("[streams] mixtral on three streams", flush=True)
+    s1, s2, s3 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    logits = dev_f32(wl.logits)
+    x = dev_bf16(wl.x)
+    y = dev_bf16(wl.y)
+    torch.cuda.synchronize()
+    idx, w = m.moe_route_topk(logits, cfg.k, stream=s1)
+    send = m.moe_dispatch_send(idx, cfg.E, cfg.R, stream=s1)
+    e1 = torch.cuda.Event()
+    e1.record(s1)
+    s2.wait_event(e1)
+    buf = m.moe_dispatch_recv(x, send.pair_row, stream=s2)
+    s3.wait_event(e1)
+    out = m.moe_combine(y, send.pair_row, w, stream=s3)
+    torch.cuda.synchronize()
+    r_idx, _, r_w32 = oracle.route_topk(wl.logits, cfg.k)
+    pr, rt = oracle.dispatch_slots(r_idx, cfg.E)
+    assert np.array_equal(host(send.pair_row), pr)
+    assert np.array_equal(host_bf16(buf), wl.x[rt])
+    ref = oracle.combine(wl.y, pr, host(w))
+    assert np.array_equal(host_bf16(out), ref)
+
+
+def test_row_kernels_loop_when_units_exceed_one_launch():
+    # H = 8 gives one 16-byte chunk per row, so units = T; T above 2^21
+    # makes the recv and combine grids loop over their units.
+    import combine_topk_route_amd as m
+
+    T, H, k = (1 << 21) + 4099, 8, 1
+    print(f"[streams] block-loop path T={T} H={H} k={k}", flush=True)
+    rng = np.random.default_rng(8)
+    x = rng.integers(0, 2**16, (T, H)).astype(np.uint16)
+    x[((x >> 7) & 0xFF) == 0xFF] &= 0x807F
+    pr = rng.permutation(T).reshape(T, k).astype(np.int32)
+    buf = m.moe_dispatch_recv(dev_bf16(x), dev_i32(pr))
+    w = np.ones((T, k), np.float32)
+    out = m.moe_combine(buf, dev_i32(pr), dev_f32(w))
+    torch.cuda.synchronize()
+    hb = host_bf16(buf)
+    expect = np.empty_like(x)
+    expect[pr[:, 0]] = x
+    assert np.array_equal(hb, expect)
+    # k = 1 with weight 1: out = x except -0 -> +0
+    assert np.array_equal(host_bf16(out), np.where(x == 0x8000, np.uint16(0), x))
