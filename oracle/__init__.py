@@ -12,6 +12,7 @@ from .moe import (  # noqa: F401
     f32_to_bf16_rne,
     fmaf,
     route_topk,
+    route_topk_grouped,
     route_topk_bruteforce,
     expert_counts,
     expert_offsets,

@@ -190,6 +190,44 @@ def route_topk(logits: np.ndarray, k: int):
     return idx.astype(np.int32), w, w.astype(np.float32)
 
 
+def route_topk_grouped(logits: np.ndarray, k: int, n_group: int, topk_group: int):
+    """Group-limited top-k routing (readings G1-G3).
+
+    The pages call Mixtral routing the special case of DeepSeek routing in
+    which the top-K group is the group of all experts ("Lower latency and
+    higher throughput with multi-node DeepSeek deployment", section "MoE
+    Router"); the group rule itself is not on the pages.  Reading: experts
+    form ``n_group`` contiguous groups of E / n_group (G1); a group's score is
+    its largest logit (G2); the ``topk_group`` best groups are kept, equal
+    scores to the lower group index, and top-k runs over the kept experts
+    with the usual ties and weights (G3: the full-E softmax renormalised over
+    the k chosen).  ``topk_group == n_group`` is plain ``route_topk``.
+    """
+    logits = np.asarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    if n_group < 1 or E % n_group:
+        raise ValueError("E must be a multiple of n_group")
+    gs = E // n_group
+    if not 1 <= topk_group <= n_group or topk_group * gs < k:
+        raise ValueError("need 1 <= topk_group <= n_group and topk_group * E/n_group >= k")
+    if not np.all(np.isfinite(logits)):
+        raise ValueError("logits must be finite")
+    gmax = logits.astype(np.float64).reshape(T, n_group, gs).max(axis=2)
+    gorder = np.argsort(-gmax + 0.0, axis=1, kind="stable")[:, :topk_group]
+    keep = np.zeros((T, n_group), dtype=bool)
+    np.put_along_axis(keep, gorder, True, axis=1)
+    keep_e = np.repeat(keep, gs, axis=1)
+    l64 = logits.astype(np.float64)
+    key = np.where(keep_e, -l64 + 0.0, np.inf)
+    idx = np.argsort(key, axis=1, kind="stable")[:, :k]
+    m = l64.max(axis=1, keepdims=True)
+    z = np.exp(l64 - m)
+    p = z / z.sum(axis=1, keepdims=True)
+    psel = np.take_along_axis(p, idx, axis=1)
+    w = psel / psel.sum(axis=1, keepdims=True)
+    return idx.astype(np.int32), w, w.astype(np.float32)
+
+
 def route_topk_bruteforce(logits: np.ndarray, k: int):
     """Exhaustive top-k for tiny E: the k-subset with the largest exact logit
     sum; among equal sums, the lexicographically smallest sorted index tuple
