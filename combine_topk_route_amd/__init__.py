@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     moe_dispatch_send,
     moe_dispatch_workspace_bytes,
     moe_route_topk,
+    moe_route_topk_grouped,
 )
 
 _lib.load()

@@ -20,6 +20,8 @@ SIGNATURES = {
     "moe_abi_version": (_c_int, []),
     "moe_strerror": (ctypes.c_char_p, [_c_int]),
     "moe_route_topk": (_c_int, [_vp, _c_i64, _c_i32, _c_i32, _vp, _vp, _vp]),
+    "moe_route_topk_grouped": (_c_int, [_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp,
+                                        _vp]),
     "moe_dispatch_workspace_bytes": (_c_size, [_c_i64, _c_i32, _c_i32]),
     "moe_dispatch_send": (_c_int, [_vp, _c_i64, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _c_size, _vp]),

@@ -75,6 +75,25 @@ def moe_route_topk(logits: torch.Tensor, k: int, topk_idx: Optional[torch.Tensor
     return topk_idx, topk_w
 
 
+def moe_route_topk_grouped(logits: torch.Tensor, k: int, n_group: int, topk_group: int,
+                           topk_idx: Optional[torch.Tensor] = None,
+                           topk_w: Optional[torch.Tensor] = None, stream=None):
+    """Group-limited top-k routing: returns (topk_idx int32 [T,k], topk_w fp32 [T,k])."""
+    lp = _dev(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    if topk_idx is None:
+        topk_idx = _empty((T, k), torch.int32, logits)
+    if topk_w is None:
+        topk_w = _empty((T, k), torch.float32, logits)
+    ip = _dev(topk_idx, "topk_idx", torch.int32)
+    wp = _dev(topk_w, "topk_w", torch.float32)
+    if topk_idx.numel() != T * k or topk_w.numel() != T * k:
+        raise ValueError("topk_idx / topk_w must hold T*k elements")
+    _check("moe_route_topk_grouped", _lib.load().moe_route_topk_grouped(
+        lp, T, E, k, n_group, topk_group, ip, wp, _stream(stream)))
+    return topk_idx, topk_w
+
+
 def moe_dispatch_workspace_bytes(T: int, E: int, k: int) -> int:
     return int(_lib.load().moe_dispatch_workspace_bytes(T, E, k))
 

@@ -57,6 +57,7 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
+constexpr int kMaxGroups = 64;  // one lane per group in the group selection
 constexpr int64_t kMaxPairs = (int64_t(1) << 31) - 1;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -207,10 +208,14 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 constexpr int kRouteWavesPerBlock = 4;
 
-template <int IPL>  // logits held per lane: ceil(E / 64) rounded up to a template size
+// IPL: logits held per lane, ceil(E / 64) rounded up to a template size.
+// GROUPED: group-limited routing; experts form n_group contiguous groups, a
+// group's score is its largest logit, and only the topk_group best groups
+// (ties to the lower group) take part in the top-k.
+template <int IPL, bool GROUPED>
 __global__ __launch_bounds__(kRouteWavesPerBlock* kWave) void route_topk_kernel(
-    const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w) {
+    const float* __restrict__ logits, int64_t T, int E, int k, int n_group, int topk_group,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
   const int lane = lane_id();
   const int64_t t = int64_t(blockIdx.x) * kRouteWavesPerBlock + threadIdx.x / kWave;
   if (t >= T) return;  // whole waves leave; no block barrier follows
@@ -252,6 +257,32 @@ __global__ __launch_bounds__(kRouteWavesPerBlock* kWave) void route_topk_kernel(
   s = wave_sum_f32(s);
 #pragma unroll
   for (int i = 0; i < IPL; ++i) pv[i] = pv[i] / s;  // fp32 softmax probabilities
+
+  if (GROUPED) {
+    const int gs = E / n_group;
+    int grp[IPL];
+#pragma unroll
+    for (int i = 0; i < IPL; ++i) grp[i] = (lane + i * kWave) / gs;
+    // Lane g ends up holding the key of group g's largest logit.
+    uint32_t gv = 0u;
+    for (int g = 0; g < n_group; ++g) {
+      uint32_t local = 0u;
+#pragma unroll
+      for (int i = 0; i < IPL; ++i) local = grp[i] == g ? max(local, key[i]) : local;
+      const uint32_t gk = wave_max_u32(local);
+      if (lane == g) gv = gk;
+    }
+    uint64_t kept = 0;
+    for (int r = 0; r < topk_group; ++r) {
+      const uint32_t best = wave_max_u32(gv);
+      const int g = __builtin_ctzll(ballot(gv == best));  // lowest group with that score
+      kept |= uint64_t(1) << g;
+      if (lane == g) gv = 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < IPL; ++i)
+      if (lane + i * kWave >= E || !((kept >> grp[i]) & 1)) key[i] = 0u;  // grp < 64 here
+  }
 
   // k rounds: the largest remaining key, then the lowest expert index that
   // holds it (expert e = lane + 64 * i, so the first item slot with a match
@@ -877,8 +908,16 @@ const char* moe_strerror(int status) {
 
 int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_idx,
                    float* topk_w, void* stream) {
+  return moe_route_topk_grouped(logits, T, E, k, 1, 1, topk_idx, topk_w, stream);
+}
+
+int moe_route_topk_grouped(const float* logits, int64_t T, int32_t E, int32_t k, int32_t n_group,
+                           int32_t topk_group, int32_t* topk_idx, float* topk_w, void* stream) {
   const int st = check_route_shape(T, E, k);
   if (st != MOE_OK) return st;
+  if (n_group < 1 || n_group > kMaxGroups || E % n_group != 0) return MOE_ERR_INVALID_ARG;
+  if (topk_group < 1 || topk_group > n_group || int64_t(topk_group) * (E / n_group) < k)
+    return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
   if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_ERR_ALIGNMENT;
@@ -886,11 +925,18 @@ int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t
   const dim3 grid(unsigned((T + kRouteWavesPerBlock - 1) / kRouteWavesPerBlock));
   const dim3 block(kRouteWavesPerBlock * kWave);
   const int ipl = (E + kWave - 1) / kWave;
-  if (ipl <= 1) return launch(route_topk_kernel<1>, grid, block, 0, s, logits, T, E, k, topk_idx, topk_w);
-  if (ipl <= 2) return launch(route_topk_kernel<2>, grid, block, 0, s, logits, T, E, k, topk_idx, topk_w);
-  if (ipl <= 4) return launch(route_topk_kernel<4>, grid, block, 0, s, logits, T, E, k, topk_idx, topk_w);
-  if (ipl <= 8) return launch(route_topk_kernel<8>, grid, block, 0, s, logits, T, E, k, topk_idx, topk_w);
-  return launch(route_topk_kernel<16>, grid, block, 0, s, logits, T, E, k, topk_idx, topk_w);
+  const bool grouped = topk_group < n_group;  // keeping every group is plain top-k
+#define MOE_ROUTE(IPL_)                                                                          \
+  return grouped ? launch(route_topk_kernel<IPL_, true>, grid, block, 0, s, logits, T, E, k,     \
+                          n_group, topk_group, topk_idx, topk_w)                                 \
+                 : launch(route_topk_kernel<IPL_, false>, grid, block, 0, s, logits, T, E, k, 1, \
+                          1, topk_idx, topk_w)
+  if (ipl <= 1) MOE_ROUTE(1);
+  if (ipl <= 2) MOE_ROUTE(2);
+  if (ipl <= 4) MOE_ROUTE(4);
+  if (ipl <= 8) MOE_ROUTE(8);
+  MOE_ROUTE(16);
+#undef MOE_ROUTE
 }
 
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k) {

@@ -92,6 +92,27 @@ int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,
                    int32_t* topk_idx, float* topk_w, void* stream);
 
 /*
+ * moe_route_topk_grouped - group-limited top-k routing.  The Mixtral router
+ * is the special case of the DeepSeek router in which the top-K group is the
+ * group of all experts ("Lower latency and higher throughput with multi-node
+ * DeepSeek deployment", section "MoE Router"); the group rule is this
+ * library's reading, as the page does not state it:
+ *   - experts form n_group contiguous groups of E / n_group;
+ *   - a group's score is its largest logit;
+ *   - the topk_group best groups are kept (equal scores: the lower group);
+ *   - top-k, ties and weights are as in moe_route_topk, over the kept
+ *     experts only; the weights are still the full-E softmax renormalised
+ *     over the k chosen.
+ * topk_group == n_group is exactly moe_route_topk.
+ * Errors: MOE_ERR_INVALID_ARG as moe_route_topk, and for n_group < 1,
+ *         n_group > 64, E % n_group != 0, topk_group outside [1, n_group],
+ *         or topk_group * (E / n_group) < k.
+ */
+int moe_route_topk_grouped(const float* logits, int64_t T, int32_t E, int32_t k,
+                           int32_t n_group, int32_t topk_group,
+                           int32_t* topk_idx, float* topk_w, void* stream);
+
+/*
  * moe_dispatch_workspace_bytes - device scratch moe_dispatch_send needs for
  * (T, E, k): per-block per-expert counts for the multi-block scan.  0 means
  * no workspace is needed (workspace may then be NULL).  Returns 0 as well for

@@ -183,3 +183,15 @@ def test_fp8_dispatch_rejects_bad_arguments(lib):
     bad = list(base)
     bad[6] = 7                       # E % R != 0
     assert f(*bad) == INVALID
+
+
+def test_grouped_route_rejects_bad_arguments(lib):
+    f = lib.moe_route_topk_grouped
+    assert f(P16, 4, 256, 8, 3, 1, P16, P16, S) == INVALID     # E % n_group != 0
+    assert f(P16, 4, 256, 8, 0, 1, P16, P16, S) == INVALID     # n_group < 1
+    assert f(P16, 4, 256, 8, 128, 2, P16, P16, S) == INVALID   # n_group > 64
+    assert f(P16, 4, 256, 8, 8, 0, P16, P16, S) == INVALID     # topk_group < 1
+    assert f(P16, 4, 256, 8, 8, 9, P16, P16, S) == INVALID     # topk_group > n_group
+    assert f(P16, 4, 256, 8, 64, 1, P16, P16, S) == INVALID    # 1 group of 4 < k = 8
+    assert f(None, 4, 256, 8, 8, 4, P16, P16, S) == INVALID
+    assert f(None, 0, 256, 8, 8, 4, None, None, S) == OK
