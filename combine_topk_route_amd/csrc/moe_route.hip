@@ -37,7 +37,8 @@
 //                        non-temporal 16-byte row loads in flight, fp32 fma
 //                        chain in j order, one bf16 RNE (v_cvt_pk_bf16_f32).
 //                        The token's rows and weights come through the scalar
-//                        cache into SGPRs.
+//                        cache into SGPRs.  For k = 1, 2, 4 a wave covers
+//                        several slices so that 16 row loads are in flight.
 //
 // There is no dense contraction here, so no MFMA: the row kernels are bound by
 // HBM bandwidth and the routing / send kernels by latency.
@@ -767,6 +768,59 @@ __global__ __launch_bounds__(kSlice) void combine_kernel(
   }
 }
 
+// Small k (1, 2, 4): one wave covers U slices of a token, so that U * K row
+// loads (16) are in flight per lane; otherwise a k = 2 wave would move only
+// 3 KiB and the launch, not the memory system, would set the pace.
+template <int K, int U>
+__global__ __launch_bounds__(kSlice) void combine_small_k_kernel(
+    const u32x4* __restrict__ y, const int32_t* __restrict__ pair_row,
+    const float* __restrict__ topk_w, int64_t T, int C, int nsb, int64_t units, int64_t capacity,
+    u32x4* __restrict__ out) {
+  for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const int64_t t = unit / nsb;
+    const int sb = int(unit - t * nsb);
+    int32_t r[K];
+    float wj[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      r[j] = pair_row[t * K + j];
+      wj[j] = topk_w[t * K + j];
+    }
+    u32x4 v[U][K];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = (sb * U + u) * kSlice + lane_id();
+#pragma unroll
+      for (int j = 0; j < K; ++j)
+        v[u][j] = (c < C && uint64_t(int64_t(r[j])) < uint64_t(capacity))
+                      ? __builtin_nontemporal_load(&y[int64_t(r[j]) * C + c])
+                      : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = (sb * U + u) * kSlice + lane_id();
+      if (c >= C) continue;
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        if (uint64_t(int64_t(r[j])) >= uint64_t(capacity)) continue;  // skipped term
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t word = v[u][j][q];
+          acc[2 * q] = __builtin_fmaf(wj[j], __uint_as_float(word << 16), acc[2 * q]);
+          acc[2 * q + 1] = __builtin_fmaf(wj[j], __uint_as_float(word & 0xFFFF0000u), acc[2 * q + 1]);
+        }
+      }
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+      out[t * C + c] = o;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -1015,11 +1069,23 @@ int moe_combine(const void* y, const int32_t* pair_row, const float* topk_w, int
   if (!aligned(pair_row, 4) || !aligned(topk_w, 4)) return MOE_ERR_ALIGNMENT;
   const int C = H / 8;
   const int ncs = (C + kSlice - 1) / kSlice;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const u32x4* yv = static_cast<const u32x4*>(y);
+  u32x4* ov = static_cast<u32x4*>(out);
+  auto small = [&](auto kern, int u) {
+    const int nsb = (ncs + u - 1) / u;
+    const int64_t units = T * nsb;
+    const unsigned nblocks = unsigned(units < kMaxRowBlocks ? units : kMaxRowBlocks);
+    return launch(kern, dim3(nblocks), dim3(kSlice), 0, s, yv, pair_row, topk_w, T, C, nsb, units,
+                  capacity, ov);
+  };
+  if (k == 1) return small(combine_small_k_kernel<1, 16>, 16);
+  if (k == 2) return small(combine_small_k_kernel<2, 8>, 8);
+  if (k == 4) return small(combine_small_k_kernel<4, 4>, 4);
   const int64_t units = T * ncs;
   const unsigned nblocks = unsigned(units < kMaxRowBlocks ? units : kMaxRowBlocks);
-  return launch(combine_kernel, dim3(nblocks), dim3(kSlice), 0, static_cast<hipStream_t>(stream),
-                static_cast<const u32x4*>(y), pair_row, topk_w, T, C, k, ncs, units, capacity,
-                static_cast<u32x4*>(out));
+  return launch(combine_kernel, dim3(nblocks), dim3(kSlice), 0, s, yv, pair_row, topk_w, T, C, k,
+                ncs, units, capacity, ov);
 }
 
 }  // extern "C"
