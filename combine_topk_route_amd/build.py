@@ -33,6 +33,32 @@ def command(out: str = LIB) -> list[str]:
     ]
 
 
+C_SMOKE_SRC = os.path.join(ROOT, "tests", "c_abi", "abi_smoke.c")
+C_SMOKE_BIN = os.path.join(ROOT, "tests", "c_abi", "abi_smoke")
+
+
+def c_smoke_command() -> list[str]:
+    """A plain C program against the C ABI (gcc; links the library and the
+    HIP runtime only for hipMalloc/hipMemcpy)."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return ["gcc", "-O2", "-std=c11", "-Wall", f"-I{INCLUDE}", f"-I{rocm}/include",
+            "-D__HIP_PLATFORM_AMD__", "-o", C_SMOKE_BIN, C_SMOKE_SRC, f"-L{PKG_DIR}",
+            "-lmoe_route", "-Wl,-rpath,$ORIGIN/../../combine_topk_route_amd", f"-L{rocm}/lib",
+            "-lamdhip64",
+            f"-Wl,-rpath,{rocm}/lib"]
+
+
+def build_c_smoke(verbose: bool = False) -> str:
+    cmd = c_smoke_command()
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("gcc failed building the C ABI smoke program")
+    return C_SMOKE_BIN
+
+
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = command(tmp)
@@ -43,6 +69,7 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed ({res.returncode}) building {LIB}")
     os.replace(tmp, LIB)
+    build_c_smoke(verbose)
     return LIB
 
 

@@ -1,0 +1,140 @@
+/*
+ * Plain C user of libmoe_route.so: no Python, no torch.
+ *
+ *   abi_smoke         host-side checks only (no device is touched): version,
+ *                     status strings, and argument validation.
+ *   abi_smoke gpu     also runs route -> dispatch -> combine on a small
+ *                     problem in device memory and checks what the method
+ *                     guarantees: counts sum to T*k, offsets are their
+ *                     exclusive scan, pair_row is a bijection onto [0, T*k)
+ *                     with row_token as its inverse, every dispatched row is
+ *                     a bit copy of its token, and combine over the dispatched
+ *                     rows (identity experts) returns the input.
+ */
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "moe_route.h"
+
+static int failures = 0;
+#define CHECK(cond)                                                   \
+  do {                                                                \
+    if (!(cond)) {                                                    \
+      fprintf(stderr, "FAIL %s:%d: %s\n", __FILE__, __LINE__, #cond); \
+      ++failures;                                                     \
+    }                                                                 \
+  } while (0)
+
+static void host_checks(void) {
+  void* p16 = (void*)(uintptr_t)0x10000; /* fake, never dereferenced */
+  CHECK(moe_abi_version() == MOE_ABI_VERSION);
+  CHECK(strcmp(moe_strerror(MOE_OK), "ok") == 0);
+  CHECK(moe_strerror(-12345) != NULL);
+  CHECK(moe_route_topk(p16, 4, 8, 9, p16, p16, NULL) == MOE_ERR_INVALID_ARG);
+  CHECK(moe_route_topk(NULL, 0, 8, 2, NULL, NULL, NULL) == MOE_OK);
+  CHECK(moe_dispatch_recv(p16, p16, 16, 255, 2, p16, 32, NULL) == MOE_ERR_ALIGNMENT);
+  CHECK(moe_dispatch_recv(p16, p16, 16, 256, 2, p16, 31, NULL) == MOE_ERR_CAPACITY);
+  CHECK(moe_combine(p16, p16, p16, 16, 256, 33, 1024, p16, NULL) == MOE_ERR_INVALID_ARG);
+  CHECK(moe_dispatch_workspace_bytes(8192, 256, 8) > 0);
+}
+
+static uint16_t bf16_of(float f) { /* round to nearest even */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+#define HIPCHECK(x) CHECK((x) == hipSuccess)
+
+static void gpu_checks(void) {
+  enum { T = 300, E = 16, K = 4, H = 256, R = 4 };
+  const int P = T * K;
+  float* logits = malloc(sizeof(float) * T * E);
+  uint16_t* x = malloc(2 * T * H);
+  uint32_t s = 12345u;
+  for (int i = 0; i < T * E; ++i) {
+    s = s * 1664525u + 1013904223u;
+    logits[i] = (float)((s >> 8) & 0xFFFF) / 4096.0f - 8.0f;
+  }
+  for (int i = 0; i < T * H; ++i) {
+    s = s * 1664525u + 1013904223u;
+    x[i] = bf16_of((float)((int)(s >> 16) - 32768) / 8192.0f);
+  }
+  float *d_logits, *d_w;
+  int32_t *d_idx, *d_counts, *d_off, *d_pr, *d_rt, *d_roff;
+  void *d_x, *d_buf, *d_out, *d_ws = NULL;
+  size_t wsb = moe_dispatch_workspace_bytes(T, E, K);
+  HIPCHECK(hipMalloc((void**)&d_logits, sizeof(float) * T * E));
+  HIPCHECK(hipMalloc((void**)&d_w, sizeof(float) * P));
+  HIPCHECK(hipMalloc((void**)&d_idx, sizeof(int32_t) * P));
+  HIPCHECK(hipMalloc((void**)&d_counts, sizeof(int32_t) * E));
+  HIPCHECK(hipMalloc((void**)&d_off, sizeof(int32_t) * (E + 1)));
+  HIPCHECK(hipMalloc((void**)&d_pr, sizeof(int32_t) * P));
+  HIPCHECK(hipMalloc((void**)&d_rt, sizeof(int32_t) * P));
+  HIPCHECK(hipMalloc((void**)&d_roff, sizeof(int32_t) * (R + 1)));
+  HIPCHECK(hipMalloc(&d_x, 2 * T * H));
+  HIPCHECK(hipMalloc(&d_buf, 2 * (size_t)P * H));
+  HIPCHECK(hipMalloc(&d_out, 2 * T * H));
+  if (wsb) HIPCHECK(hipMalloc(&d_ws, wsb));
+  HIPCHECK(hipMemcpy(d_logits, logits, sizeof(float) * T * E, hipMemcpyHostToDevice));
+  HIPCHECK(hipMemcpy(d_x, x, 2 * T * H, hipMemcpyHostToDevice));
+
+  CHECK(moe_route_topk(d_logits, T, E, K, d_idx, d_w, NULL) == MOE_OK);
+  CHECK(moe_dispatch(d_idx, d_x, T, E, K, H, R, d_counts, d_off, d_pr, d_rt, d_roff, d_buf, P, d_ws,
+                     wsb, NULL) == MOE_OK);
+  CHECK(moe_combine(d_buf, d_pr, d_w, T, H, K, P, d_out, NULL) == MOE_OK);
+  HIPCHECK(hipDeviceSynchronize());
+
+  int32_t* idx = malloc(sizeof(int32_t) * P);
+  int32_t* counts = malloc(sizeof(int32_t) * E);
+  int32_t* off = malloc(sizeof(int32_t) * (E + 1));
+  int32_t* pr = malloc(sizeof(int32_t) * P);
+  int32_t* rt = malloc(sizeof(int32_t) * P);
+  uint16_t* buf = malloc(2 * (size_t)P * H);
+  uint16_t* out = malloc(2 * T * H);
+  HIPCHECK(hipMemcpy(idx, d_idx, sizeof(int32_t) * P, hipMemcpyDeviceToHost));
+  HIPCHECK(hipMemcpy(counts, d_counts, sizeof(int32_t) * E, hipMemcpyDeviceToHost));
+  HIPCHECK(hipMemcpy(off, d_off, sizeof(int32_t) * (E + 1), hipMemcpyDeviceToHost));
+  HIPCHECK(hipMemcpy(pr, d_pr, sizeof(int32_t) * P, hipMemcpyDeviceToHost));
+  HIPCHECK(hipMemcpy(rt, d_rt, sizeof(int32_t) * P, hipMemcpyDeviceToHost));
+  HIPCHECK(hipMemcpy(buf, d_buf, 2 * (size_t)P * H, hipMemcpyDeviceToHost));
+  HIPCHECK(hipMemcpy(out, d_out, 2 * T * H, hipMemcpyDeviceToHost));
+
+  long total = 0;
+  for (int e = 0; e < E; ++e) {
+    total += counts[e];
+    CHECK(off[e + 1] - off[e] == counts[e]);
+  }
+  CHECK(total == P && off[0] == 0 && off[E] == P);
+  char* seen = calloc(P, 1);
+  for (int t = 0; t < T; ++t)
+    for (int j = 0; j < K; ++j) {
+      const int e = idx[t * K + j], r = pr[t * K + j];
+      CHECK(e >= 0 && e < E && r >= off[e] && r < off[e + 1] && !seen[r]);
+      seen[r] = 1;
+      CHECK(rt[r] == t);
+      CHECK(memcmp(buf + (size_t)r * H, x + (size_t)t * H, 2 * H) == 0);
+    }
+  for (int i = 0; i < T * H; ++i) CHECK(out[i] == (x[i] == 0x8000 ? 0 : x[i]));
+  free(seen);
+  free(idx); free(counts); free(off); free(pr); free(rt); free(buf); free(out);
+  hipFree(d_logits); hipFree(d_w); hipFree(d_idx); hipFree(d_counts); hipFree(d_off);
+  hipFree(d_pr); hipFree(d_rt); hipFree(d_roff); hipFree(d_x); hipFree(d_buf); hipFree(d_out);
+  if (d_ws) hipFree(d_ws);
+  free(logits); free(x);
+}
+
+int main(int argc, char** argv) {
+  host_checks();
+  if (argc > 1 && strcmp(argv[1], "gpu") == 0) gpu_checks();
+  if (failures) {
+    fprintf(stderr, "%d check(s) failed\n", failures);
+    return 1;
+  }
+  printf("abi_smoke ok%s\n", argc > 1 ? " (gpu)" : "");
+  return 0;
+}
