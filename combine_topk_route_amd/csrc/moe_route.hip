@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kRouteWavesPerBlock* kWave) void route_topk_kernel(
   // Softmax numerators exp(l - m).  The difference is split into its fp32
   // rounding d and the exact remainder r (TwoSum), and exp(d + r) is taken as
   // exp(d) * (1 + r): the subtraction then adds no error of its own.
-  float pv[IPL];
+  float zv[IPL];  // softmax numerators
   uint32_t key[IPL];
   float s = 0.f;
 #pragma unroll
@@ -252,12 +252,10 @@ __global__ __launch_bounds__(kRouteWavesPerBlock* kWave) void route_topk_kernel(
       z = __builtin_fmaf(ed, r, ed);
       key[i] = order_key(a);
     }
-    pv[i] = z;
+    zv[i] = z;
     s += z;
   }
-  s = wave_sum_f32(s);
-#pragma unroll
-  for (int i = 0; i < IPL; ++i) pv[i] = pv[i] / s;  // fp32 softmax probabilities
+  s = wave_sum_f32(s);  // softmax denominator over all E experts
 
   if (GROUPED) {
     const int gs = E / n_group;
@@ -287,10 +285,12 @@ __global__ __launch_bounds__(kRouteWavesPerBlock* kWave) void route_topk_kernel(
 
   // k rounds: the largest remaining key, then the lowest expert index that
   // holds it (expert e = lane + 64 * i, so the first item slot with a match
-  // and, inside it, the lowest lane).  Selected keys are zeroed.
+  // and, inside it, the lowest lane).  Selected keys are zeroed.  Only the
+  // k winners' probabilities are ever needed, so the division by the softmax
+  // denominator happens once, after the rounds, on lanes 0..k-1.
   int my_e = 0;
-  float my_p = 0.f;
-  float psum = 0.f, pcomp = 0.f;  // compensated sum of the selected probabilities
+  float my_z = 0.f;
+  float zsum = 0.f, zcomp = 0.f;  // compensated sum of the selected numerators
   for (int j = 0; j < k; ++j) {
     uint32_t best = 0u;
 #pragma unroll
@@ -307,26 +307,27 @@ __global__ __launch_bounds__(kRouteWavesPerBlock* kWave) void route_topk_kernel(
       }
     }
     const int owner = __builtin_ctzll(hit);
-    float cand = pv[0];
+    float cand = zv[0];
 #pragma unroll
-    for (int i = 1; i < IPL; ++i) cand = (i == item) ? pv[i] : cand;
-    const float pj = __uint_as_float(readlane(__float_as_uint(cand), owner));
+    for (int i = 1; i < IPL; ++i) cand = (i == item) ? zv[i] : cand;
+    const float zj = __uint_as_float(readlane(__float_as_uint(cand), owner));
 #pragma unroll
     for (int i = 0; i < IPL; ++i)
       if (i == item && lane == owner) key[i] = 0u;
     if (lane == j) {
       my_e = item * kWave + owner;
-      my_p = pj;
+      my_z = zj;
     }
-    const float ns = psum + pj;  // TwoSum of the running sum
-    const float bv = ns - psum;
-    pcomp += (psum - (ns - bv)) + (pj - bv);
-    psum = ns;
+    const float ns = zsum + zj;  // TwoSum of the running sum
+    const float bv = ns - zsum;
+    zcomp += (zsum - (ns - bv)) + (zj - bv);
+    zsum = ns;
   }
-  const float total = psum + pcomp;
   if (lane < k) {
+    const float p = my_z / s;                   // softmax probability of winner j
+    const float psel = (zsum + zcomp) / s;      // their total probability
     topk_idx[t * k + lane] = my_e;
-    topk_w[t * k + lane] = my_p / total;
+    topk_w[t * k + lane] = p / psel;            // renormalised to sum to 1
   }
 }
 
