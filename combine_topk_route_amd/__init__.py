@@ -5,6 +5,7 @@ C ABI (``include/moe_route.h``); this package is the thin torch binding.
 Importing it loads the library and fails loudly if it was not built.
 """
 from . import _lib
+from .buffers import MoeBuffers  # noqa: F401
 from .binding import (  # noqa: F401
     MoeError,
     SendResult,
