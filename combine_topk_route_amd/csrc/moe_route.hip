@@ -98,21 +98,13 @@ __device__ __forceinline__ uint32_t readlane(uint32_t v, int lane) {
 
 // Wave-wide reductions over all 64 lanes (all must be active).  The four
 // in-row steps leave every lane of a 16-lane row with the row's result; the
-// two broadcasts fold rows into lane 63, which is read into a scalar.
-__device__ __forceinline__ float wave_max_f32(float v) {
-#define MOE_STEP(CTRL, RM) \
-  v = fmaxf(v, __uint_as_float(dpp<CTRL, RM>(__float_as_uint(v), __float_as_uint(v))))
-  MOE_STEP(kDppQuad1032, 0xF);
-  MOE_STEP(kDppQuad2301, 0xF);
-  MOE_STEP(kDppRowHalfMirror, 0xF);
-  MOE_STEP(kDppRowMirror, 0xF);
-  MOE_STEP(kDppRowBcast15, 0xA);
-  MOE_STEP(kDppRowBcast31, 0xC);
-#undef MOE_STEP
-  return __uint_as_float(readlane(__float_as_uint(v), kWave - 1));
-}
+// two broadcasts fold rows into lane 63, which is read into a scalar.  The
+// `old` operand of each DPP move is the operation's identity (lanes a row
+// mask leaves out then contribute nothing), which lets the compiler fuse the
+// move into the arithmetic: one v_max_u32_dpp / v_add_f32_dpp per step.
 
-// Fixed association order, so the sum is the same on every run.
+// Fixed association order, so the sum is the same on every run (operands
+// here are non-negative, so +0.0 is an exact identity).
 __device__ __forceinline__ float wave_sum_f32(float v) {
 #define MOE_STEP(CTRL, RM) v += __uint_as_float(dpp<CTRL, RM>(0u, __float_as_uint(v)))
   MOE_STEP(kDppQuad1032, 0xF);
@@ -126,7 +118,7 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#define MOE_STEP(CTRL, RM) v = max(v, dpp<CTRL, RM>(v, v))
+#define MOE_STEP(CTRL, RM) v = max(v, dpp<CTRL, RM>(0u, v))
   MOE_STEP(kDppQuad1032, 0xF);
   MOE_STEP(kDppQuad2301, 0xF);
   MOE_STEP(kDppRowHalfMirror, 0xF);
@@ -207,6 +199,11 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of order_key on its image (a folded -0.0 comes back as +0.0).
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
 constexpr int kRouteWavesPerBlock = 4;
 
 // IPL: logits held per lane, ceil(E / 64) rounded up to a template size.
@@ -222,27 +219,29 @@ __global__ __launch_bounds__(kRouteWavesPerBlock* kWave) void route_topk_kernel(
   if (t >= T) return;  // whole waves leave; no block barrier follows
   const float* row = logits + t * E;
 
+  // Logits and their order keys (0 marks "no expert"); the maximum logit
+  // is found as the maximum key, an integer reduction.
   float lv[IPL];
-  float m = -INFINITY;
+  uint32_t key[IPL];
+  uint32_t kmax = 0u;
 #pragma unroll
   for (int i = 0; i < IPL; ++i) {
     const int e = lane + i * kWave;
-    lv[i] = e < E ? row[e] : -INFINITY;
-    m = fmaxf(m, lv[i]);
+    lv[i] = e < E ? row[e] : 0.f;
+    key[i] = e < E ? order_key(lv[i]) : 0u;
+    kmax = max(kmax, key[i]);
   }
-  m = wave_max_f32(m);
+  const float m = key_value(wave_max_u32(kmax));
 
   // Softmax numerators exp(l - m).  The difference is split into its fp32
   // rounding d and the exact remainder r (TwoSum), and exp(d + r) is taken as
   // exp(d) * (1 + r): the subtraction then adds no error of its own.
   float zv[IPL];  // softmax numerators
-  uint32_t key[IPL];
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < IPL; ++i) {
     const int e = lane + i * kWave;
     float z = 0.f;
-    key[i] = 0u;
     if (e < E) {
       const float a = lv[i], b = -m;
       const float d = a + b;
@@ -250,7 +249,6 @@ __global__ __launch_bounds__(kRouteWavesPerBlock* kWave) void route_topk_kernel(
       const float r = (a - (d - bb)) + (b - bb);
       const float ed = expf(d);
       z = __builtin_fmaf(ed, r, ed);
-      key[i] = order_key(a);
     }
     zv[i] = z;
     s += z;
@@ -648,10 +646,10 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
 
 // Maximum over the 16 lanes of each DPP row (every lane gets its row's value).
 __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
-  v = max(v, dpp<kDppQuad1032, 0xF>(v, v));
-  v = max(v, dpp<kDppQuad2301, 0xF>(v, v));
-  v = max(v, dpp<kDppRowHalfMirror, 0xF>(v, v));
-  v = max(v, dpp<kDppRowMirror, 0xF>(v, v));
+  v = max(v, dpp<kDppQuad1032, 0xF>(0u, v));
+  v = max(v, dpp<kDppQuad2301, 0xF>(0u, v));
+  v = max(v, dpp<kDppRowHalfMirror, 0xF>(0u, v));
+  v = max(v, dpp<kDppRowMirror, 0xF>(0u, v));
   return v;
 }
 
