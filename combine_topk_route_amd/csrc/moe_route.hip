@@ -316,9 +316,10 @@ __global__ __launch_bounds__(kRouteWavesPerBlock* kWave) void route_topk_kernel(
       my_e = item * kWave + owner;
       my_z = zj;
     }
-    const float ns = zsum + zj;  // TwoSum of the running sum
-    const float bv = ns - zsum;
-    zcomp += (zsum - (ns - bv)) + (zj - bv);
+    // Fast2Sum: winners come in descending order, so zsum >= zj >= 0 and the
+    // rounding error of zsum + zj is exactly zj - (ns - zsum).
+    const float ns = zsum + zj;
+    zcomp += zj - (ns - zsum);
     zsum = ns;
   }
   if (lane < k) {
@@ -436,6 +437,16 @@ __global__ __launch_bounds__(kSendThreads) void send_rank_kernel(
   int32_t* base = sm + nwaves * E;
   int32_t* scratch = base + E;
   int32_t* mat = scratch + 17;
+  int64_t a, b;
+  wave_range(P, chunk, a, b);
+  // The first step's expert indices are requested before the matrix staging
+  // below, so the two memory round trips overlap.
+  int ev0[kSendItems];
+#pragma unroll
+  for (int u = 0; u < kSendItems; ++u) {
+    const int64_t p = a + u * kWave + lane_id();
+    ev0[u] = p < b ? idx[p] : -1;
+  }
   for (int i = threadIdx.x; i < nwaves * E; i += blockDim.x) hist[i] = 0;
   if (!FUSED) {
     // The [block][expert] histogram matrix (a few KiB, L2-resident), staged
@@ -477,8 +488,6 @@ __global__ __launch_bounds__(kSendThreads) void send_rank_kernel(
     }
   }
 
-  int64_t a, b;
-  wave_range(P, chunk, a, b);
   int32_t* my_hist = hist + wid * E;
   // A wave whose range fits in one step keeps experts and local slots in
   // registers for pass 2; longer ranges park the local slot in pair_row.
@@ -490,7 +499,7 @@ __global__ __launch_bounds__(kSendThreads) void send_rank_kernel(
 #pragma unroll
     for (int u = 0; u < kSendItems; ++u) {
       const int64_t p = s0 + u * kWave + lane_id();
-      ev[u] = p < b ? idx[p] : -1;
+      ev[u] = s0 == a ? ev0[u] : (p < b ? idx[p] : -1);
     }
 #pragma unroll
     for (int u = 0; u < kSendItems; ++u) {
