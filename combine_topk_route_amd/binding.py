@@ -8,7 +8,6 @@ there is no other path.  A non-zero status raises ``MoeError``.
 """
 from __future__ import annotations
 
-import ctypes
 from typing import NamedTuple, Optional
 
 import torch

@@ -6,7 +6,6 @@ Every call below carries at least one argument the host-side checks reject
 (or T == 0), so nothing is ever enqueued.  The module is skipped where a GPU
 is visible, so that fake pointers can never reach a kernel.
 """
-import ctypes
 import os
 import re
 import subprocess

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import workloads
-from gpuhelp import dev_bf16, dev_f32, host, host_bf16
+from gpuhelp import dev_bf16, dev_f32, host_bf16
 
 pytestmark = pytest.mark.gpu
 

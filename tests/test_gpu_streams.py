@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import workloads
-from gpuhelp import DEV, assert_out_close, dev_bf16, dev_f32, dev_i32, host, host_bf16
+from gpuhelp import dev_bf16, dev_f32, dev_i32, host, host_bf16
 
 pytestmark = pytest.mark.gpu
 

@@ -8,7 +8,6 @@ import ctypes
 import ctypes.util
 
 import numpy as np
-import pytest
 import torch
 
 import oracle
