@@ -85,6 +85,10 @@ constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
 constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row -> next row
 constexpr int kDppRowBcast31 = 0x143;  // lane 31 -> rows 2 and 3
+constexpr int kDppRowShr1 = 0x111;     // row_shr:1 (lane i of a row reads lane i-1)
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
 
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
@@ -129,14 +133,21 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return readlane(v, kWave - 1);
 }
 
+// Inclusive prefix sum over the 64 lanes (all active): four shifts inside
+// each 16-lane row, then each row's running total carried into the rows
+// above it by the two row broadcasts.  Lanes a shift or a row mask leaves
+// out take the identity 0.
 __device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int32_t o = __shfl_up(v, off);
-    if (lane >= off) v += o;
-  }
-  return v;
+  uint32_t u = static_cast<uint32_t>(v);
+#define MOE_STEP(CTRL, RM) u += dpp<CTRL, RM>(0u, u)
+  MOE_STEP(kDppRowShr1, 0xF);
+  MOE_STEP(kDppRowShr2, 0xF);
+  MOE_STEP(kDppRowShr4, 0xF);
+  MOE_STEP(kDppRowShr8, 0xF);
+  MOE_STEP(kDppRowBcast15, 0xA);
+  MOE_STEP(kDppRowBcast31, 0xC);
+#undef MOE_STEP
+  return static_cast<int32_t>(u);
 }
 
 // Lanes of the wave whose `valid` lane holds the same expert id `e`
@@ -431,7 +442,7 @@ __global__ __launch_bounds__(kSendThreads) void send_rank_kernel(
     int32_t* __restrict__ pair_row, int32_t* __restrict__ row_token) {
   // LDS: [W][E] per-wave counts | [E] base | [17] scratch | [nb][E] matrix (multi-block)
   extern __shared__ int32_t sm[];
-  const int nwaves = blockDim.x / kWave;
+  constexpr int nwaves = kSendWaves;  // launched with kSendThreads
   const int wid = threadIdx.x / kWave;
   int32_t* hist = sm;
   int32_t* base = sm + nwaves * E;
@@ -477,10 +488,10 @@ __global__ __launch_bounds__(kSendThreads) void send_rank_kernel(
       const int e = threadIdx.x + q * kSendThreads;
       if (e < E) {
         int32_t tot = 0, before = 0;
-        for (int b = 0; b < nb; ++b) {
-          const int32_t c = mat[b * E + e];
+        for (int r = 0; r < nb; ++r) {
+          const int32_t c = mat[r * E + e];
           tot += c;
-          before += b < int(blockIdx.x) ? c : 0;
+          before += r < int(blockIdx.x) ? c : 0;
         }
         base[e] = tot;
         pre[q] = before;
@@ -522,11 +533,14 @@ __global__ __launch_bounds__(kSendThreads) void send_rank_kernel(
   __syncthreads();
 
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int32_t c[nwaves];
+#pragma unroll
+    for (int w = 0; w < nwaves; ++w) c[w] = hist[w * E + e];
     int32_t run = 0;
+#pragma unroll
     for (int w = 0; w < nwaves; ++w) {
-      const int32_t c = hist[w * E + e];
       hist[w * E + e] = run;
-      run += c;
+      run += c[w];
     }
     if (FUSED) base[e] = run;
   }
