@@ -27,15 +27,37 @@ def _check(fn: str, status: int) -> None:
         raise MoeError(fn, status)
 
 
-def _stream(stream) -> int:
+# The current stream's raw handle for a device index, without building a
+# torch.cuda.Stream object on every call (that costs a few microseconds, which
+# is the whole kernel time at decode sizes).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, like: torch.Tensor) -> int:
+    """The stream handle to enqueue on: `stream` if given, else the current
+    stream of the device that holds `like`."""
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        if _raw_stream is not None:
+            return _raw_stream(like.get_device())
+        return torch.cuda.current_stream(like.device).cuda_stream
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
 
 
 def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: Optional[int] = None) -> int:
+    """Device pointer of `t` after checking placement, dtype, rank and layout."""
+    try:
+        ok = (t.is_cuda and t.dtype is dtype and (ndim is None or t.dim() == ndim)
+              and t.is_contiguous())
+    except AttributeError:
+        ok = False
+    if not ok:
+        _reject(t, name, dtype, ndim)
+    return t.data_ptr()
+
+
+def _reject(t, name: str, dtype: torch.dtype, ndim: Optional[int]) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
@@ -44,9 +66,7 @@ def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: Optional[int] = N
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    return t.data_ptr()
+    raise ValueError(f"{name} must be contiguous")
 
 
 def _empty(shape, dtype, like: torch.Tensor) -> torch.Tensor:
@@ -70,7 +90,7 @@ def moe_route_topk(logits: torch.Tensor, k: int, topk_idx: Optional[torch.Tensor
     wp = _dev(topk_w, "topk_w", torch.float32)
     if topk_idx.numel() != T * k or topk_w.numel() != T * k:
         raise ValueError("topk_idx / topk_w must hold T*k elements")
-    _check("moe_route_topk", _lib.load().moe_route_topk(lp, T, E, k, ip, wp, _stream(stream)))
+    _check("moe_route_topk", _lib.load().moe_route_topk(lp, T, E, k, ip, wp, _stream(stream, logits)))
     return topk_idx, topk_w
 
 
@@ -89,7 +109,7 @@ def moe_route_topk_grouped(logits: torch.Tensor, k: int, n_group: int, topk_grou
     if topk_idx.numel() != T * k or topk_w.numel() != T * k:
         raise ValueError("topk_idx / topk_w must hold T*k elements")
     _check("moe_route_topk_grouped", _lib.load().moe_route_topk_grouped(
-        lp, T, E, k, n_group, topk_group, ip, wp, _stream(stream)))
+        lp, T, E, k, n_group, topk_group, ip, wp, _stream(stream, logits)))
     return topk_idx, topk_w
 
 
@@ -128,11 +148,13 @@ def _send_outputs(topk_idx, E, R, expert_counts, expert_offsets, pair_row, row_t
 
 
 def _workspace(T, E, k, workspace, like):
-    need = moe_dispatch_workspace_bytes(T, E, k)
-    if workspace is None and need > 0:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=like.device)
+    """(pointer, bytes, tensor) of the send workspace; allocated here when the
+    caller passed none and the launch needs one.  The library checks the size."""
     if workspace is None:
-        return 0, 0, None
+        need = moe_dispatch_workspace_bytes(T, E, k)
+        if need == 0:
+            return 0, 0, None
+        workspace = torch.empty((need,), dtype=torch.uint8, device=like.device)
     return _dev(workspace, "workspace", torch.uint8), workspace.numel(), workspace
 
 
@@ -152,7 +174,7 @@ def moe_dispatch_send(topk_idx: torch.Tensor, E: int, num_vranks: int = 1, *,
         _dev(out.expert_counts, "expert_counts", torch.int32),
         _dev(out.expert_offsets, "expert_offsets", torch.int32),
         _dev(out.pair_row, "pair_row", torch.int32),
-        _dev(out.row_token, "row_token", torch.int32), rp, wp, wn, _stream(stream)))
+        _dev(out.row_token, "row_token", torch.int32), rp, wp, wn, _stream(stream, topk_idx)))
     return out
 
 
@@ -172,7 +194,7 @@ def moe_dispatch_recv(x: torch.Tensor, pair_row: torch.Tensor, buf: Optional[tor
         raise ValueError("buf must be [>= capacity, H]")
     _check("moe_dispatch_recv", _lib.load().moe_dispatch_recv(
         xp, _dev(pair_row, "pair_row", torch.int32), T, H, k,
-        _dev(buf, "buf", torch.bfloat16), capacity, _stream(stream)))
+        _dev(buf, "buf", torch.bfloat16), capacity, _stream(stream, x)))
     return buf
 
 
@@ -203,7 +225,7 @@ def moe_dispatch(topk_idx: torch.Tensor, x: torch.Tensor, E: int, num_vranks: in
         _dev(out.expert_offsets, "expert_offsets", torch.int32),
         _dev(out.pair_row, "pair_row", torch.int32),
         _dev(out.row_token, "row_token", torch.int32), rp,
-        _dev(buf, "buf", torch.bfloat16), capacity, wp, wn, _stream(stream)))
+        _dev(buf, "buf", torch.bfloat16), capacity, wp, wn, _stream(stream, x)))
     return out, buf
 
 
@@ -236,7 +258,7 @@ def moe_dispatch_recv_fp8(x: torch.Tensor, pair_row: torch.Tensor, buf_q=None, b
     _check("moe_dispatch_recv_fp8", _lib.load().moe_dispatch_recv_fp8(
         xp, _dev(pair_row, "pair_row", torch.int32), T, H, k,
         _dev(buf_q, "buf_q", torch.uint8), _dev(buf_scale, "buf_scale", torch.float32),
-        capacity, _stream(stream)))
+        capacity, _stream(stream, x)))
     return buf_q, buf_scale
 
 
@@ -263,7 +285,7 @@ def moe_dispatch_fp8(topk_idx: torch.Tensor, x: torch.Tensor, E: int, num_vranks
         _dev(out.pair_row, "pair_row", torch.int32),
         _dev(out.row_token, "row_token", torch.int32), rp,
         _dev(buf_q, "buf_q", torch.uint8), _dev(buf_scale, "buf_scale", torch.float32),
-        capacity, wp, wn, _stream(stream)))
+        capacity, wp, wn, _stream(stream, x)))
     return out, buf_q, buf_scale
 
 
@@ -288,5 +310,5 @@ def moe_combine(y: torch.Tensor, pair_row: torch.Tensor, topk_w: torch.Tensor,
         raise ValueError("out must be [T, H]")
     _check("moe_combine", _lib.load().moe_combine(
         yp, _dev(pair_row, "pair_row", torch.int32), _dev(topk_w, "topk_w", torch.float32),
-        T, H, k, capacity, _dev(out, "out", torch.bfloat16), _stream(stream)))
+        T, H, k, capacity, _dev(out, "out", torch.bfloat16), _stream(stream, y)))
     return out
