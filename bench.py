@@ -134,23 +134,28 @@ def main() -> int:
     stream = torch.cuda.current_stream()
 
     def step(ev=None, st=None):
+        """route -> send -> recv -> combine.  Without events, send and recv go
+        through the one moe_dispatch call (same kernels, one host call fewer);
+        with events, each entry point is bracketed on its own."""
         st = stream if st is None else st
-        if ev is not None:
-            ev[0].record(st)
+        if ev is None:
+            m.moe_route_topk(logits, k, topk_idx=idx, topk_w=w, stream=st)
+            m.moe_dispatch(idx, x, E, R, buf=buf, expert_counts=counts, expert_offsets=offsets,
+                           pair_row=pair_row, row_token=row_token, rank_offsets=rank_off,
+                           workspace=ws, stream=st)
+            m.moe_combine(y, pair_row, w, out=out, stream=st)
+            return
+        ev[0].record(st)
         m.moe_route_topk(logits, k, topk_idx=idx, topk_w=w, stream=st)
-        if ev is not None:
-            ev[1].record(st)
+        ev[1].record(st)
         m.moe_dispatch_send(idx, E, R, expert_counts=counts, expert_offsets=offsets,
                             pair_row=pair_row, row_token=row_token, rank_offsets=rank_off,
                             workspace=ws, stream=st)
-        if ev is not None:
-            ev[2].record(st)
+        ev[2].record(st)
         m.moe_dispatch_recv(x, pair_row, buf=buf, stream=st)
-        if ev is not None:
-            ev[3].record(st)
+        ev[3].record(st)
         m.moe_combine(y, pair_row, w, out=out, stream=st)
-        if ev is not None:
-            ev[4].record(st)
+        ev[4].record(st)
 
     for _ in range(args.warmup):
         step()
