@@ -96,6 +96,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--no-overlap", action="store_true", help="skip the two-stream overlap timing")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache timing (keeps a kernel trace to warm launches only)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -213,8 +215,9 @@ def main() -> int:
     # preceded by a read sweep over 1 GiB that evicts L2 and the Infinity
     # Cache (a read sweep leaves no dirty lines to write back during the
     # timed launch), plus send + recv as the single moe_dispatch call.
-    flush = torch.empty((1 << 28,), dtype=torch.float32, device=dev).fill_(1.0)
-    cold_names = ["route", "dispatch_send", "dispatch_recv", "combine", "dispatch"]
+    cold_names = [] if args.no_cold else ["route", "dispatch_send", "dispatch_recv", "combine",
+                                          "dispatch"]
+    flush = torch.empty((1 << 28 if cold_names else 1,), dtype=torch.float32, device=dev).fill_(1.0)
     cold_calls = {
         "route": lambda: m.moe_route_topk(logits, k, topk_idx=idx, topk_w=w, stream=stream),
         "dispatch_send": lambda: m.moe_dispatch_send(
@@ -384,7 +387,7 @@ def main() -> int:
             "traffic": traffic,
         },
         "kernels": kernels,
-        "kernels_cold": kernels_cold,
+        "kernels_cold": kernels_cold or None,
         "fp8_dispatch_recv": fp8,
         "overlap": overlap,
         "graph_replay": None if graph_ms is None else {
