@@ -33,8 +33,8 @@ What the method computes, and where the pages state it
   on the receiving side only ("Enabling trillion-parameter models on AWS
   EFA", section "Evaluation").
 
-Readings taken where the pages are silent (each also listed in the design doc)
--------------------------------------------------------------------------
+Readings taken where the pages are silent
+-----------------------------------------
 R1  Selection is made on the fp32 logits.  Softmax is strictly increasing,
     so this equals selection on the exact probabilities; it avoids letting
     the rounding of ``exp`` decide the index set.

@@ -12,7 +12,7 @@ portable mixture-of-experts communication", section "Dispatch"; "Enabling
 trillion-parameter models on AWS EFA", section "Evaluation": fp8 block-scaled
 dispatch, bf16 combine).
 
-Readings taken where the pages are silent (also listed in the design doc):
+Readings taken where the pages are silent:
 Q1  The fp8 format is OCP E4M3 ("e4m3fn": 4 exponent bits, bias 7, 3 mantissa
     bits, no infinities, largest finite 448, NaN = S.1111.111).
 Q2  Block b of a token row holds elements [128 b, 128 b + 128); H must be a
