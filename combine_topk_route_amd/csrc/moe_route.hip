@@ -10,11 +10,16 @@
 // H200; here everything is one GPU, and the kernels are shaped for wave64,
 // DPP/ballot cross-lane operations, LDS and HBM3E:
 //
-//   route_topk_kernel    one wave per token: fp32 softmax over E logits held
-//                        in registers; k rounds of a wave-wide maximum of an
-//                        order-preserving 32-bit key (DPP row reductions, no
-//                        LDS traffic), the lowest expert index holding it
-//                        found by ballot.
+//   route_topk_kernel    16 lanes per token (32 or 64 for E > 384 or k > 16),
+//                        each holding consecutive experts: fp32 softmax over
+//                        the E logits held in registers; every lane caches
+//                        its 4 best order-preserving 32-bit keys, so each of
+//                        the k selection rounds is one DPP maximum over the
+//                        cache heads of the token's lanes.
+//   route_wave_kernel    one wave per token (group-limited routing, and plain
+//                        routing of small batches): k rounds of a wave-wide
+//                        maximum of the keys, the lowest expert index holding
+//                        it found by ballot.
 //   send_hist_kernel     per-block expert histogram; each wave groups equal
 //                        experts with ballots so the hot expert costs one LDS
 //                        update per wave, not 64.
@@ -216,13 +221,265 @@ __device__ __forceinline__ float key_value(uint32_t key) {
 }
 
 constexpr int kRouteWavesPerBlock = 4;
+constexpr int kRouteThreads = kRouteWavesPerBlock * kWave;
+constexpr int64_t kRouteWaveMaxTokens = 2048;  // up to here plain routing uses one wave per token
 
-// IPL: logits held per lane, ceil(E / 64) rounded up to a template size.
-// GROUPED: group-limited routing; experts form n_group contiguous groups, a
-// group's score is its largest logit, and only the topk_group best groups
-// (ties to the lower group) take part in the top-k.
+// Softmax numerator exp(a - m).  The difference is split into its fp32
+// rounding d and the exact remainder r (TwoSum), and exp(d + r) is taken as
+// exp(d) * (1 + r): the subtraction then adds no error of its own.
+__device__ __forceinline__ float shifted_exp(float a, float m) {
+  const float b = -m;
+  const float d = a + b;
+  const float bb = d - a;
+  const float r = (a - (d - bb)) + (b - bb);
+  const float ed = expf(d);
+  return __builtin_fmaf(ed, r, ed);
+}
+
+// Reductions over the G lanes that share one token (G = 16, 32 or 64; a
+// group starts at a multiple of G).  Every lane of the group gets the result.
+// The four in-row steps are butterflies, so each lane adds the same operands
+// in the same pairs: the sum is bit-identical across the group.
+template <int G>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+  v = max(v, dpp<kDppQuad1032, 0xF>(0u, v));
+  v = max(v, dpp<kDppQuad2301, 0xF>(0u, v));
+  v = max(v, dpp<kDppRowHalfMirror, 0xF>(0u, v));
+  v = max(v, dpp<kDppRowMirror, 0xF>(0u, v));
+  if constexpr (G == 32) {
+    v = max(v, dpp<kDppRowBcast15, 0xA>(0u, v));
+    const uint32_t lo = readlane(v, 31), hi = readlane(v, kWave - 1);
+    v = lane_id() < 32 ? lo : hi;
+  } else if constexpr (G == 64) {
+    v = max(v, dpp<kDppRowBcast15, 0xA>(0u, v));
+    v = max(v, dpp<kDppRowBcast31, 0xC>(0u, v));
+    v = readlane(v, kWave - 1);
+  }
+  return v;
+}
+
+template <int G>
+__device__ __forceinline__ float group_sum_f32(float v) {
+#define MOE_STEP(CTRL, RM) v += __uint_as_float(dpp<CTRL, RM>(0u, __float_as_uint(v)))
+  MOE_STEP(kDppQuad1032, 0xF);
+  MOE_STEP(kDppQuad2301, 0xF);
+  MOE_STEP(kDppRowHalfMirror, 0xF);
+  MOE_STEP(kDppRowMirror, 0xF);
+  if constexpr (G == 32) {
+    MOE_STEP(kDppRowBcast15, 0xA);
+    const uint32_t lo = readlane(__float_as_uint(v), 31);
+    const uint32_t hi = readlane(__float_as_uint(v), kWave - 1);
+    v = __uint_as_float(lane_id() < 32 ? lo : hi);
+  } else if constexpr (G == 64) {
+    MOE_STEP(kDppRowBcast15, 0xA);
+    MOE_STEP(kDppRowBcast31, 0xC);
+    v = __uint_as_float(readlane(__float_as_uint(v), kWave - 1));
+  }
+#undef MOE_STEP
+  return v;
+}
+
+// Error-free sum of two floats: s + e == a + b exactly (TwoSum; the result
+// does not depend on the operand order).
+__device__ __forceinline__ void two_sum(float a, float b, float& s, float& e) {
+  s = a + b;
+  const float bb = s - a;
+  e = (a - (s - bb)) + (b - bb);
+}
+
+// (s, c) <- the compensated sum over the token's G lanes of (s, c): every
+// step adds the partner's sum exactly (TwoSum) and carries the rounding
+// error in c.  Every lane of the group gets bit-identical results: the
+// in-row steps are butterflies and TwoSum is exact in either operand order,
+// and the cross-row result is read from one lane.  Lanes that a row mask
+// leaves out add (0, 0), which changes nothing.
+template <int G>
+__device__ __forceinline__ void group_sum_compensated(float& s, float& c) {
+#define MOE_STEP(CTRL, RM)                                                     \
+  {                                                                            \
+    const float os = __uint_as_float(dpp<CTRL, RM>(0u, __float_as_uint(s)));   \
+    const float oc = __uint_as_float(dpp<CTRL, RM>(0u, __float_as_uint(c)));   \
+    float e;                                                                   \
+    two_sum(s, os, s, e);                                                      \
+    c = (c + oc) + e;                                                          \
+  }
+  MOE_STEP(kDppQuad1032, 0xF);
+  MOE_STEP(kDppQuad2301, 0xF);
+  MOE_STEP(kDppRowHalfMirror, 0xF);
+  MOE_STEP(kDppRowMirror, 0xF);
+  if constexpr (G == 32) {
+    MOE_STEP(kDppRowBcast15, 0xA);
+    const bool lo = lane_id() < 32;
+    const uint32_t s_lo = readlane(__float_as_uint(s), 31), s_hi = readlane(__float_as_uint(s), 63);
+    const uint32_t c_lo = readlane(__float_as_uint(c), 31), c_hi = readlane(__float_as_uint(c), 63);
+    s = __uint_as_float(lo ? s_lo : s_hi);
+    c = __uint_as_float(lo ? c_lo : c_hi);
+  } else if constexpr (G == 64) {
+    MOE_STEP(kDppRowBcast15, 0xA);
+    MOE_STEP(kDppRowBcast31, 0xC);
+    s = __uint_as_float(readlane(__float_as_uint(s), kWave - 1));
+    c = __uint_as_float(readlane(__float_as_uint(c), kWave - 1));
+  }
+#undef MOE_STEP
+}
+
+// Insert (kv, i) into a lane's cache of its C best candidates, kept in the
+// selection order: larger key first, and among equal keys the lower item
+// (= lower expert).  Items are pushed in ascending order with strict
+// comparisons, so the lower item stays ahead on ties.
+template <int C>
+__device__ __forceinline__ void cache_push(uint32_t kv, int i, uint32_t (&h)[C], int (&hi)[C]) {
+  bool gt[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) gt[c] = kv > h[c];
+#pragma unroll
+  for (int c = C - 1; c > 0; --c) {
+    h[c] = gt[c - 1] ? h[c - 1] : (gt[c] ? kv : h[c]);
+    hi[c] = gt[c - 1] ? hi[c - 1] : (gt[c] ? i : hi[c]);
+  }
+  h[0] = gt[0] ? kv : h[0];
+  hi[0] = gt[0] ? i : hi[0];
+}
+
+// Plain top-k routing.  G lanes per token, 64 / G tokens per wave; lane g of
+// a token holds the IPL consecutive experts g*IPL .. g*IPL + IPL - 1, so a
+// lower lane always holds lower experts.  Each lane caches its C best
+// candidates in selection order; a selection round is then one group maximum
+// over the cache heads, and the lowest lane holding that maximum owns the
+// winner (the lowest expert index on ties).  The owner pops its head.  A lane
+// whose cache runs empty while it still holds candidates rescans its items
+// for the best C after the popped one; with C = 4 that needs a lane to hold
+// four of a token's winners (about 1 % of tokens at E = 256, k = 8).
+// VEC: 16-byte logit loads (IPL % 4 == 0, E % 4 == 0, 16-byte aligned rows).
+template <int G, int IPL, bool VEC>
+__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
+    const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w) {
+  constexpr int TPW = kWave / G;         // tokens per wave
+  constexpr int C = IPL < 4 ? IPL : 4;   // cached candidates per lane
+  const int lane = lane_id();
+  const int wv = threadIdx.x / kWave;
+  const int q = lane / G;  // token slot inside the wave
+  const int g = lane % G;  // lane inside the token's group
+  const int64_t t_wave = (int64_t(blockIdx.x) * kRouteWavesPerBlock + wv) * TPW;
+  if (t_wave >= T) return;  // whole waves leave; no block barrier follows
+  const int64_t t = t_wave + q;
+  const int64_t t_ld = t < T ? t : T - 1;  // lanes past T repeat the last token and store nothing
+  const int e0 = g * IPL;
+  const float* row = logits + t_ld * E + e0;
+  int32_t* idx_out = topk_idx + t_ld * k;
+
+  float lv[IPL];
+  if constexpr (VEC) {
+#pragma unroll
+    for (int v = 0; v < IPL / 4; ++v) {
+      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e0 + 4 * v < E) f = *reinterpret_cast<const float4*>(row + 4 * v);
+      lv[4 * v] = f.x;
+      lv[4 * v + 1] = f.y;
+      lv[4 * v + 2] = f.z;
+      lv[4 * v + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < IPL; ++i) lv[i] = e0 + i < E ? row[i] : 0.f;
+  }
+
+  // Order keys (0 marks "no expert"); the maximum logit is the maximum key.
+  uint32_t key[IPL];
+  uint32_t kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < IPL; ++i) {
+    key[i] = e0 + i < E ? order_key(lv[i]) : 0u;
+    kmax = max(kmax, key[i]);
+  }
+  const float m = key_value(group_max_u32<G>(kmax));
+
+  // Softmax denominator over all E experts: lane-local sum in item order,
+  // then the group's butterfly.
+  // (Lanes past E hold 0.0, a finite stand-in whose term is dropped by a
+  // select, so the loop has no branches.)
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < IPL; ++i) {
+    const float z = shifted_exp(lv[i], m);
+    s += e0 + i < E ? z : 0.f;
+  }
+  s = group_sum_f32<G>(s);
+
+  uint32_t h[C];
+  int hi[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    h[c] = 0u;
+    hi[c] = 0;
+  }
+#pragma unroll
+  for (int i = 0; i < IPL; ++i) cache_push<C>(key[i], i, h, hi);
+  int rem = E - e0 < IPL ? (E - e0 > 0 ? E - e0 : 0) : IPL;  // candidates not yet taken
+
+  uint32_t my_key = 0u;  // lane g < k: key of winner j = g
+  for (int j = 0; j < k; ++j) {
+    const uint32_t best = group_max_u32<G>(h[0]);
+    const bool hit = h[0] == best;
+    const uint64_t hits = ballot(hit);
+    bool owner = hit;
+    if (__popcll(hits) > TPW) {
+      // Some token has equal heads in several lanes: its lowest lane wins.
+      const uint64_t grp = G == kWave ? hits : (hits >> (q * G)) & ((uint64_t(1) << G) - 1);
+      owner = hit && (grp & ((uint64_t(1) << g) - 1)) == 0;
+    }
+    if (g == j) my_key = best;
+    const uint32_t kp = h[0];
+    const int ip = hi[0];
+    if (owner) {
+      if (t < T) idx_out[j] = e0 + ip;  // the owner reports winner j
+      --rem;
+#pragma unroll
+      for (int c = 0; c + 1 < C; ++c) {
+        h[c] = h[c + 1];
+        hi[c] = hi[c + 1];
+      }
+      h[C - 1] = 0u;
+    }
+    const bool refill = owner && h[0] == 0u && rem > 0 && j + 1 < k;
+    if (ballot(refill) != 0) {
+      if (refill) {
+        // The best C among the items after the popped one (kp, ip) in the
+        // selection order: smaller key, or equal key and higher item.
+#pragma unroll
+        for (int c = 0; c < C; ++c) h[c] = 0u;
+#pragma unroll
+        for (int i = 0; i < IPL; ++i) {
+          const uint32_t kv = key[i];
+          const bool after = kv < kp || (kv == kp && i > ip);
+          cache_push<C>(after ? kv : 0u, i, h, hi);
+        }
+      }
+    }
+  }
+
+  // Lane g < k of each token: numerator of winner g; the winners' total by a
+  // compensated sum over the group; the renormalised probability.  Only the
+  // k winners are divided by the softmax denominator.
+  float z = 0.f;
+  if (g < k) z = shifted_exp(key_value(my_key), m);
+  float zsum = z, zcomp = 0.f;
+  group_sum_compensated<G>(zsum, zcomp);
+  if (g < k && t < T) {
+    const float p = z / s;                   // softmax probability of winner g
+    const float psel = (zsum + zcomp) / s;   // the winners' total probability
+    topk_w[t * k + g] = p / psel;            // renormalised to sum to 1
+  }
+}
+
+// One wave per token; IPL logits per lane (expert e = lane + 64 * i).  The
+// shortest dependent chain per token, so small batches use it for plain
+// routing too.  GROUPED: group-limited routing; experts form n_group
+// contiguous groups, a group's score is its largest logit, and only the
+// topk_group best groups (ties to the lower group) take part in the top-k.
 template <int IPL, bool GROUPED>
-__global__ __launch_bounds__(kRouteWavesPerBlock* kWave) void route_topk_kernel(
+__global__ __launch_bounds__(kRouteThreads) void route_wave_kernel(
     const float* __restrict__ logits, int64_t T, int E, int k, int n_group, int topk_group,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
   const int lane = lane_id();
@@ -230,8 +487,6 @@ __global__ __launch_bounds__(kRouteWavesPerBlock* kWave) void route_topk_kernel(
   if (t >= T) return;  // whole waves leave; no block barrier follows
   const float* row = logits + t * E;
 
-  // Logits and their order keys (0 marks "no expert"); the maximum logit
-  // is found as the maximum key, an integer reduction.
   float lv[IPL];
   uint32_t key[IPL];
   uint32_t kmax = 0u;
@@ -244,25 +499,13 @@ __global__ __launch_bounds__(kRouteWavesPerBlock* kWave) void route_topk_kernel(
   }
   const float m = key_value(wave_max_u32(kmax));
 
-  // Softmax numerators exp(l - m).  The difference is split into its fp32
-  // rounding d and the exact remainder r (TwoSum), and exp(d + r) is taken as
-  // exp(d) * (1 + r): the subtraction then adds no error of its own.
   float zv[IPL];  // softmax numerators
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < IPL; ++i) {
     const int e = lane + i * kWave;
-    float z = 0.f;
-    if (e < E) {
-      const float a = lv[i], b = -m;
-      const float d = a + b;
-      const float bb = d - a;
-      const float r = (a - (d - bb)) + (b - bb);
-      const float ed = expf(d);
-      z = __builtin_fmaf(ed, r, ed);
-    }
-    zv[i] = z;
-    s += z;
+    zv[i] = e < E ? shifted_exp(lv[i], m) : 0.f;
+    s += zv[i];
   }
   s = wave_sum_f32(s);  // softmax denominator over all E experts
 
@@ -293,10 +536,10 @@ __global__ __launch_bounds__(kRouteWavesPerBlock* kWave) void route_topk_kernel(
   }
 
   // k rounds: the largest remaining key, then the lowest expert index that
-  // holds it (expert e = lane + 64 * i, so the first item slot with a match
-  // and, inside it, the lowest lane).  Selected keys are zeroed.  Only the
-  // k winners' probabilities are ever needed, so the division by the softmax
-  // denominator happens once, after the rounds, on lanes 0..k-1.
+  // holds it (the first item slot with a match and, inside it, the lowest
+  // lane).  Selected keys are zeroed.  Only the k winners' probabilities are
+  // ever needed, so the division by the softmax denominator happens once,
+  // after the rounds, on lanes 0..k-1.
   int my_e = 0;
   float my_z = 0.f;
   float zsum = 0.f, zcomp = 0.f;  // compensated sum of the selected numerators
@@ -872,6 +1115,36 @@ int check_route_shape(int64_t T, int32_t E, int32_t k) {
   return MOE_OK;
 }
 
+// Lanes per token (G) and experts per lane (IPL) of the lane-group routing
+// kernel (batches above kRouteWaveMaxTokens).  The fewest lanes per token do
+// the least work (wave-wide steps are shared by more tokens), but a lane's
+// dependent chain grows with its IPL experts: up to 128 experts 16 lanes per
+// token; above that the fewest lanes that still give the chip at least 4096
+// waves (16 per CU).  At least 32 lanes for k > 16 (lane g < k of a token
+// reports winner g), and IPL <= 24.
+struct RoutePlan {
+  int G;
+  int IPL;
+};
+
+RoutePlan plan_route(int64_t T, int E, int k) {
+  RoutePlan p{};
+  int gmin = E <= 384 ? 16 : (E <= 768 ? 32 : 64);
+  if (k > 16 && gmin < 32) gmin = 32;
+  p.G = gmin;
+  if (E > 128)
+    while (p.G < kWave && T * p.G / kWave < 4096) p.G *= 2;
+  const int need = (E + p.G - 1) / p.G;
+  const int sizes[] = {1, 2, 4, 8, 16, 24};
+  p.IPL = 24;
+  for (int v : sizes)
+    if (v >= need) {
+      p.IPL = v;
+      break;
+    }
+  return p;
+}
+
 int check_rows(int64_t T, int32_t H, int32_t k, int64_t capacity, const void* rows_in,
                const void* rows_out) {
   if (T < 0 || k < 1 || k > kMaxK || T > kMaxPairs / k) return MOE_ERR_INVALID_ARG;
@@ -998,21 +1271,52 @@ int moe_route_topk_grouped(const float* logits, int64_t T, int32_t E, int32_t k,
   if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
   if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_ERR_ALIGNMENT;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid(unsigned((T + kRouteWavesPerBlock - 1) / kRouteWavesPerBlock));
-  const dim3 block(kRouteWavesPerBlock * kWave);
-  const int ipl = (E + kWave - 1) / kWave;
+  const dim3 block(kRouteThreads);
   const bool grouped = topk_group < n_group;  // keeping every group is plain top-k
-#define MOE_ROUTE(IPL_)                                                                          \
-  return grouped ? launch(route_topk_kernel<IPL_, true>, grid, block, 0, s, logits, T, E, k,     \
+  if (grouped || T <= kRouteWaveMaxTokens) {
+    const dim3 grid(unsigned((T + kRouteWavesPerBlock - 1) / kRouteWavesPerBlock));
+    const int ipl = (E + kWave - 1) / kWave;
+#define MOE_ROUTE(IPL_)                                                                         \
+  return grouped ? launch(route_wave_kernel<IPL_, true>, grid, block, 0, s, logits, T, E, k,     \
                           n_group, topk_group, topk_idx, topk_w)                                 \
-                 : launch(route_topk_kernel<IPL_, false>, grid, block, 0, s, logits, T, E, k, 1, \
+                 : launch(route_wave_kernel<IPL_, false>, grid, block, 0, s, logits, T, E, k, 1, \
                           1, topk_idx, topk_w)
-  if (ipl <= 1) MOE_ROUTE(1);
-  if (ipl <= 2) MOE_ROUTE(2);
-  if (ipl <= 4) MOE_ROUTE(4);
-  if (ipl <= 8) MOE_ROUTE(8);
-  MOE_ROUTE(16);
+    if (ipl <= 1) MOE_ROUTE(1);
+    if (ipl <= 2) MOE_ROUTE(2);
+    if (ipl <= 4) MOE_ROUTE(4);
+    if (ipl <= 8) MOE_ROUTE(8);
+    MOE_ROUTE(16);
 #undef MOE_ROUTE
+  }
+  const RoutePlan p = plan_route(T, E, k);
+  const int64_t tokens_per_block = int64_t(kRouteWavesPerBlock) * (kWave / p.G);
+  const dim3 grid(unsigned((T + tokens_per_block - 1) / tokens_per_block));
+  const bool vec = p.IPL % 4 == 0 && E % 4 == 0 && aligned(logits, 16);
+#define MOE_ROUTE(G_, IPL_)                                                                     \
+  if (p.G == G_ && p.IPL == IPL_)                                                               \
+    return vec ? launch(route_topk_kernel<G_, IPL_, (IPL_ % 4 == 0)>, grid, block, 0, s, logits, \
+                        T, E, k, topk_idx, topk_w)                                              \
+               : launch(route_topk_kernel<G_, IPL_, false>, grid, block, 0, s, logits, T, E, k, \
+                        topk_idx, topk_w)
+  MOE_ROUTE(16, 1);
+  MOE_ROUTE(16, 2);
+  MOE_ROUTE(16, 4);
+  MOE_ROUTE(16, 8);
+  MOE_ROUTE(16, 16);
+  MOE_ROUTE(16, 24);
+  MOE_ROUTE(32, 1);
+  MOE_ROUTE(32, 2);
+  MOE_ROUTE(32, 4);
+  MOE_ROUTE(32, 8);
+  MOE_ROUTE(32, 16);
+  MOE_ROUTE(32, 24);
+  MOE_ROUTE(64, 1);
+  MOE_ROUTE(64, 2);
+  MOE_ROUTE(64, 4);
+  MOE_ROUTE(64, 8);
+  MOE_ROUTE(64, 16);
+#undef MOE_ROUTE
+  return MOE_ERR_INVALID_ARG;  // unreachable: plan_route covers every E <= 1024, k <= 32
 }
 
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k) {

@@ -23,15 +23,28 @@ def _rand_bf16(shape, seed):
     return workloads.bf16_from_f32(rng.standard_normal(shape).astype(np.float32))
 
 
+ROUTE_WAVE_MAX_TOKENS = 2048   # larger batches switch to the lane-group routing kernel
+
+
 def _route_check(logits, k):
+    """Routing of ``logits`` against the oracle, as given (a small batch:
+    one wave per token) and tiled past 2048 tokens with a ragged tail (the
+    lane-group kernel, whose lanes per token depend on T, E and k)."""
     m = _m()
-    print(f"[edges] route T={logits.shape[0]} E={logits.shape[1]} k={k}", flush=True)
-    idx, w = m.moe_route_topk(dev_f32(logits), k)
-    torch.cuda.synchronize()
-    r_idx, r_w, _ = oracle.route_topk(logits, k)
-    assert np.array_equal(host(idx), r_idx)
-    assert_weights_close(host(w), r_w)
-    return host(idx), host(w)
+    T = logits.shape[0]
+    big_T = ROUTE_WAVE_MAX_TOKENS + 53 + T % 7
+    big = np.tile(logits, (-(-big_T // T), 1))[:big_T]
+    out = None
+    for lg in ([logits, big] if T <= ROUTE_WAVE_MAX_TOKENS else [logits]):
+        print(f"[edges] route T={lg.shape[0]} E={lg.shape[1]} k={k}", flush=True)
+        idx, w = m.moe_route_topk(dev_f32(lg), k)
+        torch.cuda.synchronize()
+        r_idx, r_w, _ = oracle.route_topk(lg, k)
+        assert np.array_equal(host(idx), r_idx)
+        assert_weights_close(host(w), r_w)
+        if out is None:
+            out = host(idx), host(w)
+    return out
 
 
 # ------------------------------------------------------------------ routing
@@ -57,6 +70,34 @@ def test_route_ties_and_signed_zeros():
 def test_route_shapes(T, E, k):
     logits = np.random.default_rng(T * E + k).standard_normal((T, E)).astype(np.float32)
     _route_check(logits, k)
+
+
+@pytest.mark.parametrize("T,E,k", [(40, 500, 8), (40, 700, 12), (64, 256, 20), (9, 40, 32),
+                                   (31, 200, 5)])
+def test_route_lane_group_shapes(T, E, k):
+    """Shapes that switch the lanes per token (16, 32, 64), the experts per
+    lane and the 16-byte loads (E % 4 != 0 turns them off)."""
+    logits = np.random.default_rng(T + E * k).standard_normal((T, E)).astype(np.float32)
+    _route_check(logits, k)
+
+
+def test_route_winners_crowded_into_one_lane():
+    """Many winners held by one lane of a token (consecutive experts), with
+    ties among them: the lane's cache of best candidates empties and is
+    refilled during the k rounds."""
+    rng = np.random.default_rng(11)
+    E = 256
+    logits = rng.standard_normal((48, E)).astype(np.float32)
+    for t in range(48):
+        lo = (t % 16) * 16                       # the experts of one lane
+        logits[t, lo:lo + 16] = 5.0 + rng.integers(0, 4, 16).astype(np.float32)
+    logits[0, 0:16] = 7.0                        # one lane, all equal
+    logits[1, 16:32] = np.float32(-0.0)          # signed zeros, rest below
+    logits[1, :16] = -4.0
+    logits[1, 32:] = -4.0
+    for k in (8, 16, 20, 32):
+        idx, _ = _route_check(logits, k)
+        assert idx[0, :min(k, 16)].tolist() == list(range(min(k, 16)))
 
 
 def test_route_wide_logit_range():
