@@ -25,7 +25,8 @@ if ROOT not in sys.path:
 METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of peak), 1 MI355X"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD public spec
 SRC = os.path.join(ROOT, "combine_topk_route_amd", "csrc", "moe_route.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dsv3_prefill.txt")
+TRAFFIC_WORKLOAD = "dsv3_prefill"   # the workload the committed counter runs measured
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", f"traffic_{TRAFFIC_WORKLOAD}.txt")
 
 
 def algorithmic_bytes(cfg) -> dict:
@@ -45,9 +46,12 @@ def source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
+def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or None
-    when there are none or the kernel source changed since they were taken."""
+    when there are none for this workload or the kernel source changed since
+    they were taken."""
+    if workload != TRAFFIC_WORKLOAD:
+        return None
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.loads(f.read().split("JSON:", 1)[1].strip().splitlines()[0])
@@ -261,7 +265,7 @@ def main() -> int:
         fb = 2 * T * H + P * H + 4 * P * (H // 128) + 4 * P
         fp8 = {"us_mean": round(us, 2), "bytes": fb, "GBps": round(fb / (us * 1e-6) / 1e9, 1),
                "frac_of_peak": round(fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-               "traffic": measured_traffic("fp8_dispatch_recv"),
+               "traffic": measured_traffic("fp8_dispatch_recv", cfg.name),
                "speedup_vs_bf16_recv": None}
         del buf_q, buf_s
 
@@ -357,7 +361,7 @@ def main() -> int:
     copy_gbps = 2 * (1 << 30) * 5 / (a.elapsed_time(b) * 1e-3) / 1e9
     del src, dst
 
-    traffic = measured_traffic(dom)
+    traffic = measured_traffic(dom, cfg.name)
     rec = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),

@@ -45,19 +45,22 @@ def _stream(stream, like: torch.Tensor) -> int:
     return int(stream)
 
 
-def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: Optional[int] = None) -> int:
-    """Device pointer of `t` after checking placement, dtype, rank and layout."""
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: Optional[int] = None,
+         device: Optional[int] = None) -> int:
+    """Device pointer of `t` after checking placement, dtype, rank and layout.
+    `device`: the device index every tensor of the call must be on (the
+    first tensor's); the kernels run on that device's stream."""
     try:
         ok = (t.is_cuda and t.dtype is dtype and (ndim is None or t.dim() == ndim)
-              and t.is_contiguous())
+              and t.is_contiguous() and (device is None or t.get_device() == device))
     except AttributeError:
         ok = False
     if not ok:
-        _reject(t, name, dtype, ndim)
+        _reject(t, name, dtype, ndim, device)
     return t.data_ptr()
 
 
-def _reject(t, name: str, dtype: torch.dtype, ndim: Optional[int]) -> None:
+def _reject(t, name: str, dtype: torch.dtype, ndim: Optional[int], device: Optional[int]) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
@@ -66,6 +69,8 @@ def _reject(t, name: str, dtype: torch.dtype, ndim: Optional[int]) -> None:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if device is not None and t.get_device() != device:
+        raise ValueError(f"{name} is on cuda:{t.get_device()}, but this call runs on cuda:{device}")
     raise ValueError(f"{name} must be contiguous")
 
 
@@ -81,13 +86,14 @@ def moe_route_topk(logits: torch.Tensor, k: int, topk_idx: Optional[torch.Tensor
                    topk_w: Optional[torch.Tensor] = None, stream=None):
     """Top-k routing: returns (topk_idx int32 [T,k], topk_w fp32 [T,k])."""
     lp = _dev(logits, "logits", torch.float32, 2)
+    d = logits.get_device()
     T, E = logits.shape
     if topk_idx is None:
         topk_idx = _empty((T, k), torch.int32, logits)
     if topk_w is None:
         topk_w = _empty((T, k), torch.float32, logits)
-    ip = _dev(topk_idx, "topk_idx", torch.int32)
-    wp = _dev(topk_w, "topk_w", torch.float32)
+    ip = _dev(topk_idx, "topk_idx", torch.int32, device=d)
+    wp = _dev(topk_w, "topk_w", torch.float32, device=d)
     if topk_idx.numel() != T * k or topk_w.numel() != T * k:
         raise ValueError("topk_idx / topk_w must hold T*k elements")
     _check("moe_route_topk", _lib.load().moe_route_topk(lp, T, E, k, ip, wp, _stream(stream, logits)))
@@ -99,13 +105,14 @@ def moe_route_topk_grouped(logits: torch.Tensor, k: int, n_group: int, topk_grou
                            topk_w: Optional[torch.Tensor] = None, stream=None):
     """Group-limited top-k routing: returns (topk_idx int32 [T,k], topk_w fp32 [T,k])."""
     lp = _dev(logits, "logits", torch.float32, 2)
+    d = logits.get_device()
     T, E = logits.shape
     if topk_idx is None:
         topk_idx = _empty((T, k), torch.int32, logits)
     if topk_w is None:
         topk_w = _empty((T, k), torch.float32, logits)
-    ip = _dev(topk_idx, "topk_idx", torch.int32)
-    wp = _dev(topk_w, "topk_w", torch.float32)
+    ip = _dev(topk_idx, "topk_idx", torch.int32, device=d)
+    wp = _dev(topk_w, "topk_w", torch.float32, device=d)
     if topk_idx.numel() != T * k or topk_w.numel() != T * k:
         raise ValueError("topk_idx / topk_w must hold T*k elements")
     _check("moe_route_topk_grouped", _lib.load().moe_route_topk_grouped(
@@ -155,7 +162,18 @@ def _workspace(T, E, k, workspace, like):
         if need == 0:
             return 0, 0, None
         workspace = torch.empty((need,), dtype=torch.uint8, device=like.device)
-    return _dev(workspace, "workspace", torch.uint8), workspace.numel(), workspace
+    return (_dev(workspace, "workspace", torch.uint8, device=like.get_device()), workspace.numel(),
+            workspace)
+
+
+def _send_ptrs(out: "SendResult", d: int):
+    """Device pointers of the send outputs (rank_offsets may be None)."""
+    rp = (_dev(out.rank_offsets, "rank_offsets", torch.int32, device=d)
+          if out.rank_offsets is not None else None)
+    return (_dev(out.expert_counts, "expert_counts", torch.int32, device=d),
+            _dev(out.expert_offsets, "expert_offsets", torch.int32, device=d),
+            _dev(out.pair_row, "pair_row", torch.int32, device=d),
+            _dev(out.row_token, "row_token", torch.int32, device=d), rp)
 
 
 def moe_dispatch_send(topk_idx: torch.Tensor, E: int, num_vranks: int = 1, *,
@@ -164,17 +182,14 @@ def moe_dispatch_send(topk_idx: torch.Tensor, E: int, num_vranks: int = 1, *,
                       stream=None) -> SendResult:
     """Counts, offsets and the stable destination row of every (token, j) pair."""
     ip = _dev(topk_idx, "topk_idx", torch.int32, 2)
+    d = topk_idx.get_device()
     T, k = topk_idx.shape
     out = _send_outputs(topk_idx, E, num_vranks, expert_counts, expert_offsets, pair_row,
                         row_token, rank_offsets, with_rank_offsets)
     wp, wn, _ = _workspace(T, E, k, workspace, topk_idx)
-    rp = _dev(out.rank_offsets, "rank_offsets", torch.int32) if out.rank_offsets is not None else None
+    cp, op, pp, tp, rp = _send_ptrs(out, d)
     _check("moe_dispatch_send", _lib.load().moe_dispatch_send(
-        ip, T, E, k, num_vranks,
-        _dev(out.expert_counts, "expert_counts", torch.int32),
-        _dev(out.expert_offsets, "expert_offsets", torch.int32),
-        _dev(out.pair_row, "pair_row", torch.int32),
-        _dev(out.row_token, "row_token", torch.int32), rp, wp, wn, _stream(stream, topk_idx)))
+        ip, T, E, k, num_vranks, cp, op, pp, tp, rp, wp, wn, _stream(stream, topk_idx)))
     return out
 
 
@@ -192,9 +207,10 @@ def moe_dispatch_recv(x: torch.Tensor, pair_row: torch.Tensor, buf: Optional[tor
         capacity = buf.shape[0]
     if buf.dim() != 2 or buf.shape[1] != H or buf.shape[0] < capacity:
         raise ValueError("buf must be [>= capacity, H]")
+    d = x.get_device()
     _check("moe_dispatch_recv", _lib.load().moe_dispatch_recv(
-        xp, _dev(pair_row, "pair_row", torch.int32), T, H, k,
-        _dev(buf, "buf", torch.bfloat16), capacity, _stream(stream, x)))
+        xp, _dev(pair_row, "pair_row", torch.int32, device=d), T, H, k,
+        _dev(buf, "buf", torch.bfloat16, device=d), capacity, _stream(stream, x)))
     return buf
 
 
@@ -204,7 +220,8 @@ def moe_dispatch(topk_idx: torch.Tensor, x: torch.Tensor, E: int, num_vranks: in
                  workspace=None, stream=None):
     """Send then receive on one stream; returns (SendResult, buf)."""
     ip = _dev(topk_idx, "topk_idx", torch.int32, 2)
-    xp = _dev(x, "x", torch.bfloat16, 2)
+    d = topk_idx.get_device()
+    xp = _dev(x, "x", torch.bfloat16, 2, device=d)
     T, k = topk_idx.shape
     H = x.shape[1]
     if x.shape[0] != T:
@@ -218,14 +235,10 @@ def moe_dispatch(topk_idx: torch.Tensor, x: torch.Tensor, E: int, num_vranks: in
     if buf.dim() != 2 or buf.shape[1] != H or buf.shape[0] < capacity:
         raise ValueError("buf must be [>= capacity, H]")
     wp, wn, _ = _workspace(T, E, k, workspace, topk_idx)
-    rp = _dev(out.rank_offsets, "rank_offsets", torch.int32) if out.rank_offsets is not None else None
+    cp, op, pp, tp, rp = _send_ptrs(out, d)
     _check("moe_dispatch", _lib.load().moe_dispatch(
-        ip, xp, T, E, k, H, num_vranks,
-        _dev(out.expert_counts, "expert_counts", torch.int32),
-        _dev(out.expert_offsets, "expert_offsets", torch.int32),
-        _dev(out.pair_row, "pair_row", torch.int32),
-        _dev(out.row_token, "row_token", torch.int32), rp,
-        _dev(buf, "buf", torch.bfloat16), capacity, wp, wn, _stream(stream, x)))
+        ip, xp, T, E, k, H, num_vranks, cp, op, pp, tp, rp,
+        _dev(buf, "buf", torch.bfloat16, device=d), capacity, wp, wn, _stream(stream, x)))
     return out, buf
 
 
@@ -255,10 +268,11 @@ def moe_dispatch_recv_fp8(x: torch.Tensor, pair_row: torch.Tensor, buf_q=None, b
         raise ValueError("pair_row must be [T, k]")
     k = pair_row.shape[1]
     buf_q, buf_scale, capacity = _fp8_bufs(x, T, k, buf_q, buf_scale, capacity)
+    d = x.get_device()
     _check("moe_dispatch_recv_fp8", _lib.load().moe_dispatch_recv_fp8(
-        xp, _dev(pair_row, "pair_row", torch.int32), T, H, k,
-        _dev(buf_q, "buf_q", torch.uint8), _dev(buf_scale, "buf_scale", torch.float32),
-        capacity, _stream(stream, x)))
+        xp, _dev(pair_row, "pair_row", torch.int32, device=d), T, H, k,
+        _dev(buf_q, "buf_q", torch.uint8, device=d),
+        _dev(buf_scale, "buf_scale", torch.float32, device=d), capacity, _stream(stream, x)))
     return buf_q, buf_scale
 
 
@@ -268,7 +282,8 @@ def moe_dispatch_fp8(topk_idx: torch.Tensor, x: torch.Tensor, E: int, num_vranks
                      with_rank_offsets: bool = True, workspace=None, stream=None):
     """Send then fp8 receive on one stream; returns (SendResult, buf_q, buf_scale)."""
     ip = _dev(topk_idx, "topk_idx", torch.int32, 2)
-    xp = _dev(x, "x", torch.bfloat16, 2)
+    d = topk_idx.get_device()
+    xp = _dev(x, "x", torch.bfloat16, 2, device=d)
     T, k = topk_idx.shape
     H = x.shape[1]
     if x.shape[0] != T:
@@ -277,15 +292,12 @@ def moe_dispatch_fp8(topk_idx: torch.Tensor, x: torch.Tensor, E: int, num_vranks
                         row_token, rank_offsets, with_rank_offsets)
     buf_q, buf_scale, capacity = _fp8_bufs(x, T, k, buf_q, buf_scale, capacity)
     wp, wn, _ = _workspace(T, E, k, workspace, topk_idx)
-    rp = _dev(out.rank_offsets, "rank_offsets", torch.int32) if out.rank_offsets is not None else None
+    cp, op, pp, tp, rp = _send_ptrs(out, d)
     _check("moe_dispatch_fp8", _lib.load().moe_dispatch_fp8(
-        ip, xp, T, E, k, H, num_vranks,
-        _dev(out.expert_counts, "expert_counts", torch.int32),
-        _dev(out.expert_offsets, "expert_offsets", torch.int32),
-        _dev(out.pair_row, "pair_row", torch.int32),
-        _dev(out.row_token, "row_token", torch.int32), rp,
-        _dev(buf_q, "buf_q", torch.uint8), _dev(buf_scale, "buf_scale", torch.float32),
-        capacity, wp, wn, _stream(stream, x)))
+        ip, xp, T, E, k, H, num_vranks, cp, op, pp, tp, rp,
+        _dev(buf_q, "buf_q", torch.uint8, device=d),
+        _dev(buf_scale, "buf_scale", torch.float32, device=d), capacity, wp, wn,
+        _stream(stream, x)))
     return out, buf_q, buf_scale
 
 
@@ -308,7 +320,9 @@ def moe_combine(y: torch.Tensor, pair_row: torch.Tensor, topk_w: torch.Tensor,
         out = _empty((T, H), torch.bfloat16, y)
     if out.shape != (T, H):
         raise ValueError("out must be [T, H]")
+    d = y.get_device()
     _check("moe_combine", _lib.load().moe_combine(
-        yp, _dev(pair_row, "pair_row", torch.int32), _dev(topk_w, "topk_w", torch.float32),
-        T, H, k, capacity, _dev(out, "out", torch.bfloat16), _stream(stream, y)))
+        yp, _dev(pair_row, "pair_row", torch.int32, device=d),
+        _dev(topk_w, "topk_w", torch.float32, device=d), T, H, k, capacity,
+        _dev(out, "out", torch.bfloat16, device=d), _stream(stream, y)))
     return out

@@ -1,0 +1,35 @@
+"""bench.py's host-side pieces (no GPU): the algorithmic byte counts the
+roofline uses, the counter-traffic lookup, and the one-GPU guard."""
+import os
+import subprocess
+import sys
+
+import bench
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_algorithmic_bytes_at_dsv3_prefill():
+    cfg = workloads.CONFIGS["dsv3_prefill"]
+    b = bench.algorithmic_bytes(cfg)
+    T, H, k = cfg.T, cfg.H, cfg.k
+    # per token: 2H(k+1) bytes of rows, plus 4 (recv) or 8 (combine) bytes per pair
+    assert b["dispatch_recv"] == T * (2 * H * (k + 1) + 4 * k) == 1_057_226_752
+    assert b["combine"] == T * (2 * H * (k + 1) + 8 * k) == 1_057_488_896
+    assert b["route"] == T * (4 * cfg.E + 8 * k)
+
+
+def test_traffic_is_only_reported_for_the_measured_workload_and_source():
+    assert bench.measured_traffic("combine", "kimi_k2") is None
+    got = bench.measured_traffic("combine", bench.TRAFFIC_WORKLOAD)
+    if got is not None:  # the committed counters match the current kernel source
+        alg = bench.algorithmic_bytes(workloads.CONFIGS[bench.TRAFFIC_WORKLOAD])["combine"]
+        assert 1.0 <= got / alg < 1.05
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
