@@ -27,7 +27,8 @@
 //                        inside a wave (mbcnt), exclusive prefix across waves
 //                        (LDS), and across blocks from the histogram matrix,
 //                        which every block scans for itself.  Small inputs run
-//                        histogram, scan and slots in one block.
+//                        histogram, scan and slots in one block of 8 or 16
+//                        waves.
 //   dispatch_recv_kernel one block per (token, 1 KiB column slice); each wave
 //                        copies the slice to one of the token's k rows: a
 //                        cached 16-byte load (the block's waves share it) and
@@ -592,6 +593,11 @@ constexpr int kSendThreads = 512;
 constexpr int kSendWaves = kSendThreads / kWave;
 constexpr int kSendItems = 4;  // pair indices each lane loads before processing them
 constexpr int64_t kSendFusedMaxPairs = 4096;
+// Above one 8-wave step (2048 pairs) the single block would park slots in
+// memory for a second step; a 16-wave block keeps them in registers (its
+// per-wave counts take 16 * E ints of LDS, hence the limit on E).
+constexpr int kSendWideThreads = 1024;
+constexpr int kSendWideMaxE = 512;
 constexpr int64_t kSendChunkTarget = 2048;
 constexpr int kSendMaxBlocks = 64;
 constexpr int kSendMatrixInts = 8192;  // [block][expert] counts staged in LDS by the rank kernel
@@ -599,6 +605,7 @@ constexpr int kLdsInts = 16384;        // 64 KiB of LDS per block at most
 
 struct SendPlan {
   bool fused;
+  int threads;    // of the single fused block: kSendThreads or kSendWideThreads
   int nb;         // blocks of the histogram and rank kernels
   int64_t chunk;  // pairs per block
   size_t ws_bytes;
@@ -607,7 +614,9 @@ struct SendPlan {
 SendPlan plan_send(int64_t P, int E) {
   SendPlan p{};
   if (P <= kSendFusedMaxPairs) {
+    const bool one_step = P <= int64_t(kSendWaves) * kWave * kSendItems;
     p.fused = true;
+    p.threads = !one_step && E <= kSendWideMaxE ? kSendWideThreads : kSendThreads;
     p.nb = 1;
     p.chunk = P > 0 ? P : 1;
     p.ws_bytes = 0;
@@ -677,15 +686,15 @@ __global__ __launch_bounds__(kSendThreads) void send_hist_kernel(const int32_t* 
 // come from the per-block histogram matrix (multi-block) or from the wave
 // counts themselves (FUSED, one block).  Pass 2 adds the exclusive prefix
 // over waves and the block base, and writes row_token.
-template <bool FUSED>
-__global__ __launch_bounds__(kSendThreads) void send_rank_kernel(
+template <bool FUSED, int THREADS, int ITEMS>
+__global__ __launch_bounds__(THREADS) void send_rank_kernel(
     const int32_t* __restrict__ idx, int64_t P, int E, int k, int nbits, int64_t chunk, int nb,
     const int32_t* __restrict__ ws_cnt, int L, int R, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ rank_offsets,
     int32_t* __restrict__ pair_row, int32_t* __restrict__ row_token) {
   // LDS: [W][E] per-wave counts | [E] base | [17] scratch | [nb][E] matrix (multi-block)
   extern __shared__ int32_t sm[];
-  constexpr int nwaves = kSendWaves;  // launched with kSendThreads
+  constexpr int nwaves = THREADS / kWave;  // launched with THREADS threads (at most 16 waves)
   const int wid = threadIdx.x / kWave;
   int32_t* hist = sm;
   int32_t* base = sm + nwaves * E;
@@ -695,9 +704,9 @@ __global__ __launch_bounds__(kSendThreads) void send_rank_kernel(
   wave_range(P, chunk, a, b);
   // The first step's expert indices are requested before the matrix staging
   // below, so the two memory round trips overlap.
-  int ev0[kSendItems];
+  int ev0[ITEMS];
 #pragma unroll
-  for (int u = 0; u < kSendItems; ++u) {
+  for (int u = 0; u < ITEMS; ++u) {
     const int64_t p = a + u * kWave + lane_id();
     ev0[u] = p < b ? idx[p] : -1;
   }
@@ -707,16 +716,16 @@ __global__ __launch_bounds__(kSendThreads) void send_rank_kernel(
     // with batches of independent coalesced loads.
     constexpr int kBatch = 16;
     const int n = nb * E;
-    for (int i0 = threadIdx.x; i0 < n; i0 += kSendThreads * kBatch) {
+    for (int i0 = threadIdx.x; i0 < n; i0 += THREADS * kBatch) {
       int32_t v[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        const int i = i0 + u * kSendThreads;
+        const int i = i0 + u * THREADS;
         v[u] = i < n ? ws_cnt[i] : 0;
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        const int i = i0 + u * kSendThreads;
+        const int i = i0 + u * THREADS;
         if (i < n) mat[i] = v[u];
       }
     }
@@ -728,7 +737,7 @@ __global__ __launch_bounds__(kSendThreads) void send_rank_kernel(
   if (!FUSED) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int e = threadIdx.x + q * kSendThreads;
+      const int e = threadIdx.x + q * THREADS;
       if (e < E) {
         int32_t tot = 0, before = 0;
         for (int r = 0; r < nb; ++r) {
@@ -745,18 +754,18 @@ __global__ __launch_bounds__(kSendThreads) void send_rank_kernel(
   int32_t* my_hist = hist + wid * E;
   // A wave whose range fits in one step keeps experts and local slots in
   // registers for pass 2; longer ranges park the local slot in pair_row.
-  const bool one_step = b - a <= int64_t(kWave) * kSendItems;
-  int keep_e[kSendItems];
-  int32_t keep_slot[kSendItems];
-  for (int64_t s0 = a; s0 < b; s0 += kWave * kSendItems) {
-    int ev[kSendItems];
+  const bool one_step = b - a <= int64_t(kWave) * ITEMS;
+  int keep_e[ITEMS];
+  int32_t keep_slot[ITEMS];
+  for (int64_t s0 = a; s0 < b; s0 += kWave * ITEMS) {
+    int ev[ITEMS];
 #pragma unroll
-    for (int u = 0; u < kSendItems; ++u) {
+    for (int u = 0; u < ITEMS; ++u) {
       const int64_t p = s0 + u * kWave + lane_id();
       ev[u] = s0 == a ? ev0[u] : (p < b ? idx[p] : -1);
     }
 #pragma unroll
-    for (int u = 0; u < kSendItems; ++u) {
+    for (int u = 0; u < ITEMS; ++u) {
       const int64_t p = s0 + u * kWave + lane_id();
       const int e = ev[u];
       const bool valid = uint32_t(e) < uint32_t(E);
@@ -805,23 +814,23 @@ __global__ __launch_bounds__(kSendThreads) void send_rank_kernel(
   if (!FUSED) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int e = threadIdx.x + q * kSendThreads;
+      const int e = threadIdx.x + q * THREADS;
       if (e < E) base[e] += pre[q];
     }
     __syncthreads();
   }
 
-  for (int64_t s0 = a; s0 < b; s0 += kWave * kSendItems) {
+  for (int64_t s0 = a; s0 < b; s0 += kWave * ITEMS) {
     if (!one_step) {
 #pragma unroll
-      for (int u = 0; u < kSendItems; ++u) {
+      for (int u = 0; u < ITEMS; ++u) {
         const int64_t p = s0 + u * kWave + lane_id();
         keep_e[u] = p < b ? idx[p] : -1;
         keep_slot[u] = p < b ? pair_row[p] : -1;
       }
     }
 #pragma unroll
-    for (int u = 0; u < kSendItems; ++u) {
+    for (int u = 0; u < ITEMS; ++u) {
       const int64_t p = s0 + u * kWave + lane_id();
       if (p < b) {
         const int e = keep_e[u];
@@ -1190,18 +1199,25 @@ int enqueue_send(const int32_t* topk_idx, int64_t T, int32_t E, int32_t k, int32
   const SendPlan plan = plan_send(P, E);
   const int nbits = nbits_for(E);
   const int L = E / R;
-  const size_t lds = (size_t(kSendWaves) * E + E + 17 + (plan.fused ? 0 : size_t(plan.nb) * E)) *
+  const int waves = plan.fused ? plan.threads / kWave : kSendWaves;
+  const size_t lds = (size_t(waves) * E + E + 17 + (plan.fused ? 0 : size_t(plan.nb) * E)) *
                      sizeof(int32_t);
   if (plan.fused) {
-    return launch(send_rank_kernel<true>, dim3(1), dim3(kSendThreads), lds, st, topk_idx, P, E, k,
-                  nbits, plan.chunk, 1, static_cast<const int32_t*>(nullptr), L, R, counts,
-                  offsets, rank_offsets, pair_row, row_token);
+    const int32_t* none = nullptr;
+    if (plan.threads == kSendWideThreads)
+      return launch(send_rank_kernel<true, kSendWideThreads, kSendItems>, dim3(1),
+                    dim3(kSendWideThreads), lds, st, topk_idx, P, E, k, nbits, plan.chunk, 1, none,
+                    L, R, counts, offsets, rank_offsets, pair_row, row_token);
+    return launch(send_rank_kernel<true, kSendThreads, kSendItems>, dim3(1), dim3(kSendThreads),
+                  lds, st, topk_idx, P, E, k, nbits, plan.chunk, 1, none, L, R, counts, offsets,
+                  rank_offsets, pair_row, row_token);
   }
   int32_t* ws = static_cast<int32_t*>(workspace);
   const int rc = launch(send_hist_kernel, dim3(plan.nb), dim3(kSendThreads), size_t(E) * 4, st,
                         topk_idx, P, E, nbits, plan.chunk, ws);
   if (rc != MOE_OK) return rc;
-  return launch(send_rank_kernel<false>, dim3(plan.nb), dim3(kSendThreads), lds, st, topk_idx, P,
+  return launch(send_rank_kernel<false, kSendThreads, kSendItems>, dim3(plan.nb),
+                dim3(kSendThreads), lds, st, topk_idx, P,
                 E, k, nbits, plan.chunk, plan.nb, static_cast<const int32_t*>(ws), L, R, counts,
                 offsets, rank_offsets, pair_row, row_token);
 }

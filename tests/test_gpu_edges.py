@@ -128,6 +128,10 @@ def _send_check(idx, E, R):
 @pytest.mark.parametrize("T,k,E,R", [
     (1, 1, 1, 1),          # one pair
     (16, 2, 8, 1),
+    (256, 8, 256, 32),     # P = 2048: largest one-step 8-wave block
+    (2049, 1, 64, 4),      # P = 2049: 16-wave single block, ragged wave ranges
+    (300, 8, 512, 16),     # P = 2400: 16-wave block at its largest E
+    (400, 8, 1024, 8),     # P = 3200, E > 512: 8-wave block in two steps
     (512, 8, 256, 32),     # P = 4096: largest single-block case
     (513, 8, 256, 32),     # P = 4104: first multi-block case, ragged last block
     (3001, 3, 7, 7),       # odd sizes, small E
