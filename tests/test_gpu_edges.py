@@ -170,7 +170,8 @@ def test_send_drops_out_of_range_experts():
 # ------------------------------------------------------------------ recv / combine
 
 @pytest.mark.parametrize("T,H,k", [(1, 8, 1), (3, 8, 2), (37, 296, 3), (1000, 4096, 2),
-                                   (129, 7168, 8), (5, 520, 10), (64, 1024, 32), (300, 64, 4)])
+                                   (129, 7168, 8), (5, 520, 10), (64, 1024, 32), (300, 64, 4),
+                                   (3, 1 << 20, 2), (2, 1 << 20, 8)])   # the widest rows allowed
 def test_recv_and_combine_ragged_shapes(T, H, k):
     m = _m()
     print(f"[edges] recv/combine T={T} H={H} k={k}", flush=True)
