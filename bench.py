@@ -135,20 +135,23 @@ def main() -> int:
     rank_off = torch.empty((R + 1,), dtype=torch.int32, device=dev)
     ws = torch.empty((max(1, m.moe_dispatch_workspace_bytes(T, E, k)),), dtype=torch.uint8,
                      device=dev)
+    rws = torch.zeros((m.moe_route_dispatch_workspace_bytes(T, E, k),), dtype=torch.uint8,
+                      device=dev)
     buf = torch.empty((P, H), dtype=torch.bfloat16, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(ev=None, st=None):
-        """route -> send -> recv -> combine.  Without events, send and recv go
-        through the one moe_dispatch call (same kernels, one host call fewer);
-        with events, each entry point is bracketed on its own."""
+        """route -> send -> recv -> combine.  Without events, route, send and
+        recv go through the one moe_route_dispatch call (the same kernels,
+        route and send in one launch for small batches) and combine through
+        moe_combine; with events, each entry point is bracketed on its own."""
         st = stream if st is None else st
         if ev is None:
-            m.moe_route_topk(logits, k, topk_idx=idx, topk_w=w, stream=st)
-            m.moe_dispatch(idx, x, E, R, buf=buf, expert_counts=counts, expert_offsets=offsets,
-                           pair_row=pair_row, row_token=row_token, rank_offsets=rank_off,
-                           workspace=ws, stream=st)
+            m.moe_route_dispatch(logits, x, k, R, topk_idx=idx, topk_w=w, buf=buf,
+                                 expert_counts=counts, expert_offsets=offsets, pair_row=pair_row,
+                                 row_token=row_token, rank_offsets=rank_off, workspace=rws,
+                                 stream=st)
             m.moe_combine(y, pair_row, w, out=out, stream=st)
             return
         ev[0].record(st)

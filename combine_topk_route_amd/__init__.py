@@ -17,6 +17,8 @@ from .binding import (  # noqa: F401
     moe_dispatch_recv,
     moe_dispatch_send,
     moe_dispatch_workspace_bytes,
+    moe_route_dispatch,
+    moe_route_dispatch_workspace_bytes,
     moe_route_topk,
     moe_route_topk_grouped,
 )

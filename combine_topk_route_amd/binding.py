@@ -242,6 +242,54 @@ def moe_dispatch(topk_idx: torch.Tensor, x: torch.Tensor, E: int, num_vranks: in
     return out, buf
 
 
+def moe_route_dispatch_workspace_bytes(T: int, E: int, k: int) -> int:
+    return int(_lib.load().moe_route_dispatch_workspace_bytes(T, E, k))
+
+
+def moe_route_dispatch(logits: torch.Tensor, x: torch.Tensor, k: int, num_vranks: int = 1, *,
+                       topk_idx=None, topk_w=None, buf=None, capacity=None, expert_counts=None,
+                       expert_offsets=None, pair_row=None, row_token=None, rank_offsets=None,
+                       with_rank_offsets: bool = True, workspace=None, stream=None):
+    """Route, send and receive in one call; returns (topk_idx, topk_w,
+    SendResult, buf).  ``workspace`` (uint8, at least
+    moe_route_dispatch_workspace_bytes bytes) must start zeroed the first time
+    it is used; it is allocated zeroed here when not given.  Keep one
+    workspace per stream and do not pass it to the other dispatch calls."""
+    lp = _dev(logits, "logits", torch.float32, 2)
+    d = logits.get_device()
+    xp = _dev(x, "x", torch.bfloat16, 2, device=d)
+    T, E = logits.shape
+    H = x.shape[1]
+    if x.shape[0] != T:
+        raise ValueError("x and logits disagree on T")
+    if topk_idx is None:
+        topk_idx = _empty((T, k), torch.int32, logits)
+    if topk_w is None:
+        topk_w = _empty((T, k), torch.float32, logits)
+    if topk_idx.shape != (T, k) or topk_w.shape != (T, k):
+        raise ValueError("topk_idx / topk_w must be [T, k]")
+    ip = _dev(topk_idx, "topk_idx", torch.int32, device=d)
+    wp = _dev(topk_w, "topk_w", torch.float32, device=d)
+    out = _send_outputs(topk_idx, E, num_vranks, expert_counts, expert_offsets, pair_row,
+                        row_token, rank_offsets, with_rank_offsets)
+    if buf is None:
+        buf = _empty((T * k if capacity is None else capacity, H), torch.bfloat16, x)
+    if capacity is None:
+        capacity = buf.shape[0]
+    if buf.dim() != 2 or buf.shape[1] != H or buf.shape[0] < capacity:
+        raise ValueError("buf must be [>= capacity, H]")
+    if workspace is None:
+        workspace = torch.zeros((max(1, moe_route_dispatch_workspace_bytes(T, E, k)),),
+                                dtype=torch.uint8, device=logits.device)
+    wsp = _dev(workspace, "workspace", torch.uint8, device=d)
+    cp, op, pp, tp, rp = _send_ptrs(out, d)
+    _check("moe_route_dispatch", _lib.load().moe_route_dispatch(
+        lp, xp, T, E, k, H, num_vranks, ip, wp, cp, op, pp, tp, rp,
+        _dev(buf, "buf", torch.bfloat16, device=d), capacity, wsp, workspace.numel(),
+        _stream(stream, logits)))
+    return topk_idx, topk_w, out, buf
+
+
 def _fp8_bufs(x, T, k, buf_q, buf_scale, capacity):
     H = x.shape[1]
     rows = T * k if capacity is None else capacity

@@ -42,6 +42,10 @@ class MoeBuffers:
         self.row_token = torch.empty((cap,), dtype=i32, device=dev)
         ws = _b.moe_dispatch_workspace_bytes(max_tokens, num_experts, k)
         self.workspace = torch.empty((max(ws, 1),), dtype=torch.uint8, device=dev)
+        # route_dispatch's own workspace: its leading arrival counter starts at
+        # zero and every call leaves it at zero.
+        rws = _b.moe_route_dispatch_workspace_bytes(max_tokens, num_experts, k)
+        self.route_workspace = torch.zeros((max(rws, 1),), dtype=torch.uint8, device=dev)
         self.buf = torch.empty((cap, hidden), dtype=torch.bfloat16, device=dev)
         self.out = torch.empty((max_tokens, hidden), dtype=torch.bfloat16, device=dev)
         self.buf_q = self.buf_scale = None
@@ -75,6 +79,19 @@ class MoeBuffers:
                         pair_row=s.pair_row, row_token=s.row_token, rank_offsets=s.rank_offsets,
                         workspace=self.workspace, stream=stream)
         return s, self.buf[: T * self.k]
+
+    def route_dispatch(self, logits: torch.Tensor, x: torch.Tensor, stream=None):
+        """Route + send + receive in one call; returns (topk_idx, topk_w,
+        SendResult, buf [T*k, H])."""
+        T = self._t(x.shape[0])
+        s = self._send(T)
+        _b.moe_route_dispatch(logits, x, self.k, self.R, topk_idx=self.topk_idx[:T],
+                              topk_w=self.topk_w[:T], buf=self.buf[: T * self.k],
+                              expert_counts=s.expert_counts, expert_offsets=s.expert_offsets,
+                              pair_row=s.pair_row, row_token=s.row_token,
+                              rank_offsets=s.rank_offsets, workspace=self.route_workspace,
+                              stream=stream)
+        return self.topk_idx[:T], self.topk_w[:T], s, self.buf[: T * self.k]
 
     def dispatch_fp8(self, topk_idx: torch.Tensor, x: torch.Tensor, stream=None):
         """Send + fp8 receive; returns (SendResult, codes [T*k, H], scales [T*k, H/128])."""

@@ -479,13 +479,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
 // routing too.  GROUPED: group-limited routing; experts form n_group
 // contiguous groups, a group's score is its largest logit, and only the
 // topk_group best groups (ties to the lower group) take part in the top-k.
+// Routing of token t by the calling wave (all 64 lanes active).
 template <int IPL, bool GROUPED>
-__global__ __launch_bounds__(kRouteThreads) void route_wave_kernel(
-    const float* __restrict__ logits, int64_t T, int E, int k, int n_group, int topk_group,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+__device__ __forceinline__ void route_wave_token(const float* __restrict__ logits, int64_t t, int E,
+                                                 int k, int n_group, int topk_group,
+                                                 int32_t* __restrict__ topk_idx,
+                                                 float* __restrict__ topk_w) {
   const int lane = lane_id();
-  const int64_t t = int64_t(blockIdx.x) * kRouteWavesPerBlock + threadIdx.x / kWave;
-  if (t >= T) return;  // whole waves leave; no block barrier follows
   const float* row = logits + t * E;
 
   float lv[IPL];
@@ -585,6 +585,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_wave_kernel(
   }
 }
 
+template <int IPL, bool GROUPED>
+__global__ __launch_bounds__(kRouteThreads) void route_wave_kernel(
+    const float* __restrict__ logits, int64_t T, int E, int k, int n_group, int topk_group,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  const int64_t t = int64_t(blockIdx.x) * kRouteWavesPerBlock + threadIdx.x / kWave;
+  if (t >= T) return;  // whole waves leave; no block barrier follows
+  route_wave_token<IPL, GROUPED>(logits, t, E, k, n_group, topk_group, topk_idx, topk_w);
+}
+
 // ---------------------------------------------------------------------------
 // dispatch send: histogram, scan, stable slots
 // ---------------------------------------------------------------------------
@@ -639,11 +648,12 @@ SendPlan plan_send(int64_t P, int E) {
   return p;
 }
 
-// The pairs [a, b) this wave handles inside its block's chunk.
-__device__ __forceinline__ void wave_range(int64_t P, int64_t chunk, int64_t& a, int64_t& b) {
+// The pairs [a, b) this wave handles inside chunk `bid`.
+__device__ __forceinline__ void wave_range(int64_t P, int64_t chunk, int bid, int64_t& a,
+                                           int64_t& b) {
   const int nwaves = blockDim.x / kWave;
   const int wid = threadIdx.x / kWave;
-  const int64_t c0 = int64_t(blockIdx.x) * chunk;
+  const int64_t c0 = int64_t(bid) * chunk;
   const int64_t c1 = c0 + chunk < P ? c0 + chunk : P;
   int64_t per = (c1 - c0 + nwaves - 1) / nwaves;
   per = (per + kWave - 1) / kWave * kWave;
@@ -659,7 +669,7 @@ __global__ __launch_bounds__(kSendThreads) void send_hist_kernel(const int32_t* 
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
   int64_t a, b;
-  wave_range(P, chunk, a, b);
+  wave_range(P, chunk, blockIdx.x, a, b);
   for (int64_t s0 = a; s0 < b; s0 += kWave * kSendItems) {
     int ev[kSendItems];
 #pragma unroll
@@ -686,14 +696,15 @@ __global__ __launch_bounds__(kSendThreads) void send_hist_kernel(const int32_t* 
 // come from the per-block histogram matrix (multi-block) or from the wave
 // counts themselves (FUSED, one block).  Pass 2 adds the exclusive prefix
 // over waves and the block base, and writes row_token.
+// The rank step of block `bid` (0 for FUSED), run by a block of THREADS
+// threads; sm: its dynamic LDS.
 template <bool FUSED, int THREADS, int ITEMS>
-__global__ __launch_bounds__(THREADS) void send_rank_kernel(
-    const int32_t* __restrict__ idx, int64_t P, int E, int k, int nbits, int64_t chunk, int nb,
-    const int32_t* __restrict__ ws_cnt, int L, int R, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ rank_offsets,
+__device__ __forceinline__ void send_rank_block(
+    int bid, int32_t* sm, const int32_t* __restrict__ idx, int64_t P, int E, int k, int nbits,
+    int64_t chunk, int nb, const int32_t* __restrict__ ws_cnt, int L, int R,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ rank_offsets,
     int32_t* __restrict__ pair_row, int32_t* __restrict__ row_token) {
   // LDS: [W][E] per-wave counts | [E] base | [17] scratch | [nb][E] matrix (multi-block)
-  extern __shared__ int32_t sm[];
   constexpr int nwaves = THREADS / kWave;  // launched with THREADS threads (at most 16 waves)
   const int wid = threadIdx.x / kWave;
   int32_t* hist = sm;
@@ -701,7 +712,7 @@ __global__ __launch_bounds__(THREADS) void send_rank_kernel(
   int32_t* scratch = base + E;
   int32_t* mat = scratch + 17;
   int64_t a, b;
-  wave_range(P, chunk, a, b);
+  wave_range(P, chunk, bid, a, b);
   // The first step's expert indices are requested before the matrix staging
   // below, so the two memory round trips overlap.
   int ev0[ITEMS];
@@ -743,7 +754,7 @@ __global__ __launch_bounds__(THREADS) void send_rank_kernel(
         for (int r = 0; r < nb; ++r) {
           const int32_t c = mat[r * E + e];
           tot += c;
-          before += r < int(blockIdx.x) ? c : 0;
+          before += r < bid ? c : 0;
         }
         base[e] = tot;
         pre[q] = before;
@@ -799,7 +810,7 @@ __global__ __launch_bounds__(THREADS) void send_rank_kernel(
   __syncthreads();
   // base[e]: total pairs of expert e -> exclusive offsets.
   const int32_t total = block_excl_scan(base, E, scratch);
-  if (FUSED || blockIdx.x == 0) {
+  if (FUSED || bid == 0) {
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
       offsets[e] = base[e];
       counts[e] = (e + 1 < E ? base[e + 1] : total) - base[e];
@@ -843,6 +854,61 @@ __global__ __launch_bounds__(THREADS) void send_rank_kernel(
       }
     }
   }
+}
+
+template <bool FUSED, int THREADS, int ITEMS>
+__global__ __launch_bounds__(THREADS) void send_rank_kernel(
+    const int32_t* __restrict__ idx, int64_t P, int E, int k, int nbits, int64_t chunk, int nb,
+    const int32_t* __restrict__ ws_cnt, int L, int R, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ rank_offsets,
+    int32_t* __restrict__ pair_row, int32_t* __restrict__ row_token) {
+  extern __shared__ int32_t sm[];
+  send_rank_block<FUSED, THREADS, ITEMS>(blockIdx.x, sm, idx, P, E, k, nbits, chunk, nb, ws_cnt,
+                                         L, R, counts, offsets, rank_offsets, pair_row, row_token);
+}
+
+// ---------------------------------------------------------------------------
+// route + send in one launch for small batches
+// ---------------------------------------------------------------------------
+
+// Every block routes THREADS / 64 tokens, one wave each, then counts itself
+// in on `arrivals` after a device-scope fence.  The block that arrives last
+// sees every token's routing and runs the single-block send; it then resets
+// the counter for the next call on the stream.  No block ever waits for
+// another, so the grid drains whatever the residency.
+template <int IPL, int THREADS>
+__global__ __launch_bounds__(THREADS) void route_send_kernel(
+    const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, uint32_t* __restrict__ arrivals, int nbits, int L, int R,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ pair_row,
+    int32_t* __restrict__ row_token) {
+  extern __shared__ int32_t sm[];
+  __shared__ int32_t is_last;
+  const int64_t t = int64_t(blockIdx.x) * (THREADS / kWave) + threadIdx.x / kWave;
+  if (t < T) route_wave_token<IPL, false>(logits, t, E, k, 1, 1, topk_idx, topk_w);
+  // Release the block's routing at device scope before it counts in: each
+  // wave for its own stores, then thread 0 for all that the barrier ordered
+  // before it.  The last block to arrive acquires, so it sees every block's
+  // routing.  (Release and acquire only: a full fence would write the L2
+  // back a second time.)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint32_t before =
+        __hip_atomic_fetch_add(arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = before == gridDim.x - 1;
+    if (is_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  if (!is_last) return;  // the whole block leaves
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int64_t P = T * k;
+  send_rank_block<true, THREADS, kSendItems>(0, sm, topk_idx, P, E, k, nbits, P, 1, nullptr, L, R,
+                                             counts, offsets, rank_offsets, pair_row, row_token);
+  if (threadIdx.x == 0)  // every block has counted in: ready for the next call on the stream
+    __hip_atomic_store(arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -1154,6 +1220,56 @@ RoutePlan plan_route(int64_t T, int E, int k) {
   return p;
 }
 
+int enqueue_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t n_group,
+                  int32_t topk_group, int32_t* topk_idx, float* topk_w, hipStream_t s) {
+  const dim3 block(kRouteThreads);
+  const bool grouped = topk_group < n_group;  // keeping every group is plain top-k
+  if (grouped || T <= kRouteWaveMaxTokens) {
+    const dim3 grid(unsigned((T + kRouteWavesPerBlock - 1) / kRouteWavesPerBlock));
+    const int ipl = (E + kWave - 1) / kWave;
+#define MOE_ROUTE(IPL_)                                                                         \
+  return grouped ? launch(route_wave_kernel<IPL_, true>, grid, block, 0, s, logits, T, E, k,     \
+                          n_group, topk_group, topk_idx, topk_w)                                 \
+                 : launch(route_wave_kernel<IPL_, false>, grid, block, 0, s, logits, T, E, k, 1, \
+                          1, topk_idx, topk_w)
+    if (ipl <= 1) MOE_ROUTE(1);
+    if (ipl <= 2) MOE_ROUTE(2);
+    if (ipl <= 4) MOE_ROUTE(4);
+    if (ipl <= 8) MOE_ROUTE(8);
+    MOE_ROUTE(16);
+#undef MOE_ROUTE
+  }
+  const RoutePlan p = plan_route(T, E, k);
+  const int64_t tokens_per_block = int64_t(kRouteWavesPerBlock) * (kWave / p.G);
+  const dim3 grid(unsigned((T + tokens_per_block - 1) / tokens_per_block));
+  const bool vec = p.IPL % 4 == 0 && E % 4 == 0 && aligned(logits, 16);
+#define MOE_ROUTE(G_, IPL_)                                                                     \
+  if (p.G == G_ && p.IPL == IPL_)                                                               \
+    return vec ? launch(route_topk_kernel<G_, IPL_, (IPL_ % 4 == 0)>, grid, block, 0, s, logits, \
+                        T, E, k, topk_idx, topk_w)                                              \
+               : launch(route_topk_kernel<G_, IPL_, false>, grid, block, 0, s, logits, T, E, k, \
+                        topk_idx, topk_w)
+  MOE_ROUTE(16, 1);
+  MOE_ROUTE(16, 2);
+  MOE_ROUTE(16, 4);
+  MOE_ROUTE(16, 8);
+  MOE_ROUTE(16, 16);
+  MOE_ROUTE(16, 24);
+  MOE_ROUTE(32, 1);
+  MOE_ROUTE(32, 2);
+  MOE_ROUTE(32, 4);
+  MOE_ROUTE(32, 8);
+  MOE_ROUTE(32, 16);
+  MOE_ROUTE(32, 24);
+  MOE_ROUTE(64, 1);
+  MOE_ROUTE(64, 2);
+  MOE_ROUTE(64, 4);
+  MOE_ROUTE(64, 8);
+  MOE_ROUTE(64, 16);
+#undef MOE_ROUTE
+  return MOE_ERR_INVALID_ARG;  // unreachable: plan_route covers every E <= 1024, k <= 32
+}
+
 int check_rows(int64_t T, int32_t H, int32_t k, int64_t capacity, const void* rows_in,
                const void* rows_out) {
   if (T < 0 || k < 1 || k > kMaxK || T > kMaxPairs / k) return MOE_ERR_INVALID_ARG;
@@ -1253,6 +1369,43 @@ int enqueue_recv_fp8(const void* x, const int32_t* pair_row, int64_t T, int32_t 
                 static_cast<uint8_t*>(buf_q), buf_s, capacity);
 }
 
+// Workspace of moe_route_dispatch: the arrival counter of the fused route +
+// send launch, then the send workspace.
+constexpr size_t kArrivalBytes = 256;
+
+bool route_send_fusable(int64_t T, int32_t E, int32_t k) {
+  return T <= kRouteWaveMaxTokens && plan_send(T * k, E).fused;
+}
+
+int enqueue_route_send(const float* logits, int64_t T, int32_t E, int32_t k, int32_t R,
+                       int32_t* topk_idx, float* topk_w, uint32_t* arrivals, int32_t* counts,
+                       int32_t* offsets, int32_t* pair_row, int32_t* row_token,
+                       int32_t* rank_offsets, hipStream_t st) {
+  const SendPlan plan = plan_send(T * k, E);
+  const int waves = plan.threads / kWave;
+  const size_t lds = (size_t(waves) * E + E + 17) * sizeof(int32_t);
+  const dim3 grid(unsigned((T + waves - 1) / waves));
+  const int ipl = (E + kWave - 1) / kWave;
+  const int nbits = nbits_for(E);
+  const int L = E / R;
+#define MOE_FUSED(IPL_, THR_)                                                                  \
+  return launch(route_send_kernel<IPL_, THR_>, grid, dim3(THR_), lds, st, logits, T, E, k,     \
+                topk_idx, topk_w, arrivals, nbits, L, R, counts, offsets, rank_offsets,        \
+                pair_row, row_token)
+#define MOE_FUSED_IPL(THR_)        \
+  if (ipl <= 1) MOE_FUSED(1, THR_); \
+  if (ipl <= 2) MOE_FUSED(2, THR_); \
+  if (ipl <= 4) MOE_FUSED(4, THR_); \
+  if (ipl <= 8) MOE_FUSED(8, THR_); \
+  MOE_FUSED(16, THR_)
+  if (plan.threads == kSendWideThreads) {
+    MOE_FUSED_IPL(kSendWideThreads);
+  }
+  MOE_FUSED_IPL(kSendThreads);
+#undef MOE_FUSED_IPL
+#undef MOE_FUSED
+}
+
 }  // namespace
 
 extern "C" {
@@ -1286,53 +1439,8 @@ int moe_route_topk_grouped(const float* logits, int64_t T, int32_t E, int32_t k,
   if (T == 0) return MOE_OK;
   if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
   if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_ERR_ALIGNMENT;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 block(kRouteThreads);
-  const bool grouped = topk_group < n_group;  // keeping every group is plain top-k
-  if (grouped || T <= kRouteWaveMaxTokens) {
-    const dim3 grid(unsigned((T + kRouteWavesPerBlock - 1) / kRouteWavesPerBlock));
-    const int ipl = (E + kWave - 1) / kWave;
-#define MOE_ROUTE(IPL_)                                                                         \
-  return grouped ? launch(route_wave_kernel<IPL_, true>, grid, block, 0, s, logits, T, E, k,     \
-                          n_group, topk_group, topk_idx, topk_w)                                 \
-                 : launch(route_wave_kernel<IPL_, false>, grid, block, 0, s, logits, T, E, k, 1, \
-                          1, topk_idx, topk_w)
-    if (ipl <= 1) MOE_ROUTE(1);
-    if (ipl <= 2) MOE_ROUTE(2);
-    if (ipl <= 4) MOE_ROUTE(4);
-    if (ipl <= 8) MOE_ROUTE(8);
-    MOE_ROUTE(16);
-#undef MOE_ROUTE
-  }
-  const RoutePlan p = plan_route(T, E, k);
-  const int64_t tokens_per_block = int64_t(kRouteWavesPerBlock) * (kWave / p.G);
-  const dim3 grid(unsigned((T + tokens_per_block - 1) / tokens_per_block));
-  const bool vec = p.IPL % 4 == 0 && E % 4 == 0 && aligned(logits, 16);
-#define MOE_ROUTE(G_, IPL_)                                                                     \
-  if (p.G == G_ && p.IPL == IPL_)                                                               \
-    return vec ? launch(route_topk_kernel<G_, IPL_, (IPL_ % 4 == 0)>, grid, block, 0, s, logits, \
-                        T, E, k, topk_idx, topk_w)                                              \
-               : launch(route_topk_kernel<G_, IPL_, false>, grid, block, 0, s, logits, T, E, k, \
-                        topk_idx, topk_w)
-  MOE_ROUTE(16, 1);
-  MOE_ROUTE(16, 2);
-  MOE_ROUTE(16, 4);
-  MOE_ROUTE(16, 8);
-  MOE_ROUTE(16, 16);
-  MOE_ROUTE(16, 24);
-  MOE_ROUTE(32, 1);
-  MOE_ROUTE(32, 2);
-  MOE_ROUTE(32, 4);
-  MOE_ROUTE(32, 8);
-  MOE_ROUTE(32, 16);
-  MOE_ROUTE(32, 24);
-  MOE_ROUTE(64, 1);
-  MOE_ROUTE(64, 2);
-  MOE_ROUTE(64, 4);
-  MOE_ROUTE(64, 8);
-  MOE_ROUTE(64, 16);
-#undef MOE_ROUTE
-  return MOE_ERR_INVALID_ARG;  // unreachable: plan_route covers every E <= 1024, k <= 32
+  return enqueue_route(logits, T, E, k, n_group, topk_group, topk_idx, topk_w,
+                       static_cast<hipStream_t>(stream));
 }
 
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k) {
@@ -1372,6 +1480,45 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int64_t T, int32_t E, i
   const hipStream_t s = static_cast<hipStream_t>(stream);
   st = enqueue_send(topk_idx, T, E, k, num_vranks, expert_counts, expert_offsets, pair_row,
                     row_token, rank_offsets, workspace, s);
+  if (st != MOE_OK) return st;
+  return enqueue_recv(x, pair_row, T, H, k, buf, capacity, s);
+}
+
+size_t moe_route_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k) {
+  if (check_route_shape(T, E, k) != MOE_OK) return 0;
+  return kArrivalBytes + plan_send(T * k, E).ws_bytes;
+}
+
+int moe_route_dispatch(const float* logits, const void* x, int64_t T, int32_t E, int32_t k,
+                       int32_t H, int32_t num_vranks, int32_t* topk_idx, float* topk_w,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* pair_row,
+                       int32_t* row_token, int32_t* rank_offsets, void* buf, int64_t capacity,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_route_shape(T, E, k);
+  if (st != MOE_OK) return st;
+  if (T > 0 && (!logits || !topk_idx || !topk_w)) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)))
+    return MOE_ERR_ALIGNMENT;
+  const size_t send_ws = workspace_bytes > kArrivalBytes ? workspace_bytes - kArrivalBytes : 0;
+  char* ws = static_cast<char*>(workspace);
+  st = check_send(topk_idx, T, E, k, num_vranks, expert_counts, expert_offsets, pair_row,
+                  row_token, rank_offsets, ws ? ws + kArrivalBytes : nullptr, send_ws);
+  if (st != MOE_OK) return st;
+  st = check_rows(T, H, k, capacity, x, buf);
+  if (st != MOE_OK || T == 0) return st;
+  if (workspace == nullptr || workspace_bytes < kArrivalBytes) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, 4)) return MOE_ERR_ALIGNMENT;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (route_send_fusable(T, E, k)) {
+    st = enqueue_route_send(logits, T, E, k, num_vranks, topk_idx, topk_w,
+                            static_cast<uint32_t*>(workspace), expert_counts, expert_offsets,
+                            pair_row, row_token, rank_offsets, s);
+  } else {
+    st = enqueue_route(logits, T, E, k, 1, 1, topk_idx, topk_w, s);
+    if (st == MOE_OK)
+      st = enqueue_send(topk_idx, T, E, k, num_vranks, expert_counts, expert_offsets, pair_row,
+                        row_token, rank_offsets, ws + kArrivalBytes, s);
+  }
   if (st != MOE_OK) return st;
   return enqueue_recv(x, pair_row, T, H, k, buf, capacity, s);
 }

@@ -189,6 +189,46 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int64_t T, int32_t E,
                  size_t workspace_bytes, void* stream);
 
 /*
+ * moe_route_dispatch - moe_route_topk, moe_dispatch_send and
+ * moe_dispatch_recv on one stream, in one call: the router's top-K output
+ * goes straight into dispatch ("Efficient and portable mixture-of-experts
+ * communication", sections "Introduction" and "Dispatch"; "Lower latency and
+ * higher throughput with multi-node DeepSeek deployment", section "MoE
+ * Router").  Arguments are the union of the three calls', with the same
+ * meaning; topk_idx and topk_w are outputs.  All are checked before anything
+ * is enqueued.  The outputs are identical to the three separate calls.
+ *
+ * Small batches (T <= 2048 and T*k <= 4096) route and send in one launch:
+ * the last routing block to finish runs the single-block send, found with an
+ * arrival counter at the start of the workspace.
+ *
+ *   workspace  moe_route_dispatch_workspace_bytes(T, E, k) bytes (4-byte
+ *              aligned).  Its first 4 bytes must be zero before the first
+ *              call that uses it (e.g. hipMemset, torch.zeros); every call
+ *              leaves them zero again.  Calls that share a workspace must be
+ *              ordered on one stream, and it must not be passed to the other
+ *              dispatch calls, whose workspace use would overwrite the
+ *              counter.
+ * Errors: as the three calls; MOE_ERR_WORKSPACE for a NULL or short
+ *         workspace (T > 0).
+ */
+int moe_route_dispatch(const float* logits, const void* x, int64_t T, int32_t E,
+                       int32_t k, int32_t H, int32_t num_vranks,
+                       int32_t* topk_idx, float* topk_w,
+                       int32_t* expert_counts, int32_t* expert_offsets,
+                       int32_t* pair_row, int32_t* row_token, int32_t* rank_offsets,
+                       void* buf, int64_t capacity, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * moe_route_dispatch_workspace_bytes - the workspace moe_route_dispatch
+ * needs for (T, E, k): a 256-byte arrival counter block followed by the
+ * moe_dispatch_send workspace.  Returns 0 for arguments moe_route_topk would
+ * reject.
+ */
+size_t moe_route_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k);
+
+/*
  * moe_dispatch_recv_fp8 - moe_dispatch_recv with block-scaled fp8 payloads:
  * each token row is quantised on the fly with one scale per 128-element block
  * and the fp8 row plus its scales are written to the token's k rows

@@ -194,3 +194,35 @@ def test_grouped_route_rejects_bad_arguments(lib):
     assert f(P16, 4, 256, 8, 64, 1, P16, P16, S) == INVALID    # 1 group of 4 < k = 8
     assert f(None, 4, 256, 8, 8, 4, P16, P16, S) == INVALID
     assert f(None, 0, 256, 8, 8, 4, None, None, S) == OK
+
+
+def test_route_dispatch_checks_every_part_before_enqueueing(lib):
+    f = lib.moe_route_dispatch
+    wsf = lib.moe_route_dispatch_workspace_bytes
+    assert wsf(128, 256, 8) == 256                 # the arrival counter block only
+    assert wsf(8192, 256, 8) == 256 + lib.moe_dispatch_workspace_bytes(8192, 256, 8)
+    assert wsf(8192, 0, 8) == 0
+    ws = wsf(8192, 256, 8)
+    # logits, x, T, E, k, H, R, idx, w, counts, offsets, pair_row, row_token, rank, buf, cap, ws, wsb
+    base = [P16, P16, 8192, 256, 8, 7168, 32, P16, P16, P16, P16, P16, P16, None, P16, 8192 * 8,
+            P16, ws, S]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a4=33) == INVALID                  # k > 32 (routing)
+    assert call(a0=None) == INVALID               # null logits
+    assert call(a8=None) == INVALID               # null weights
+    assert call(a0=P16 + 2) == ALIGN              # misaligned logits
+    assert call(a6=5) == INVALID                  # E % R != 0 (send)
+    assert call(a15=8192 * 8 - 1) == CAP          # capacity < T*k (recv)
+    assert call(a5=7170) == ALIGN                 # H % 8 != 0
+    assert call(a16=None) == WS                   # no workspace
+    assert call(a17=ws - 1) == WS                 # short: the send part does not fit
+    assert call(a2=128, a15=1024, a17=255) == WS  # short: no room for the counter
+    assert call(a2=128, a15=1024, a17=256, a16=P16 + 2) == ALIGN
+    assert call(a2=0, a0=None, a1=None, a7=None, a8=None, a9=None, a10=None, a11=None, a12=None,
+                a14=None, a15=0, a16=None, a17=0) == OK

@@ -1,0 +1,134 @@
+"""moe_route_dispatch (route + send + recv in one call; small batches route
+and send in one launch) against the separate calls and the oracle: every
+output bit-identical, the workspace's arrival counter back at zero after
+every call, and graph replays equal to eager calls."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpuhelp import DEV, dev_bf16, dev_f32, host, host_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _m():
+    import combine_topk_route_amd as m
+
+    return m
+
+
+def _separate(m, logits, x, k, E, R):
+    idx, w = m.moe_route_topk(logits, k)
+    send, buf = m.moe_dispatch(idx, x, E, R)
+    return idx, w, send, buf
+
+
+def _same(a, b):
+    ia, wa, sa, ba = a
+    ib, wb, sb, bb = b
+    assert torch.equal(ia, ib)
+    assert torch.equal(wa.view(torch.int32), wb.view(torch.int32))
+    for u, v in zip(sa, sb):
+        assert torch.equal(u, v)
+    assert torch.equal(ba.view(torch.int16), bb.view(torch.int16))
+
+
+def _inputs(T, E, H, seed):
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    x = workloads.bf16_from_f32(rng.standard_normal((T, H)).astype(np.float32))
+    return logits, x
+
+
+@pytest.mark.parametrize("name", list(workloads.CONFIGS))
+def test_route_dispatch_matches_separate_calls_and_oracle(name):
+    m = _m()
+    wl = workloads.make(name, seed=3, with_y=False)
+    cfg = wl.cfg
+    print(f"\n[route_dispatch] {name} T={cfg.T} E={cfg.E} k={cfg.k}", flush=True)
+    logits, x = dev_f32(wl.logits), dev_bf16(wl.x)
+    got = m.moe_route_dispatch(logits, x, cfg.k, cfg.R)
+    ref = _separate(m, logits, x, cfg.k, cfg.E, cfg.R)
+    torch.cuda.synchronize()
+    _same(got, ref)
+    r_idx, _, _ = oracle.route_topk(wl.logits, cfg.k)
+    r_pr, r_rt = oracle.dispatch_slots(r_idx, cfg.E)
+    assert np.array_equal(host(got[0]), r_idx)
+    assert np.array_equal(host(got[2].pair_row), r_pr)
+    assert np.array_equal(host(got[2].row_token), r_rt)
+    rows = np.random.default_rng(1).choice(cfg.P, min(cfg.P, 512), replace=False)
+    assert np.array_equal(host_bf16(got[3][torch.from_numpy(rows).to(DEV)]), wl.x[r_rt[rows]])
+
+
+@pytest.mark.parametrize("T,E,k,R", [
+    (1, 8, 2, 1), (5, 8, 8, 2), (7, 256, 8, 32),       # ragged single blocks
+    (256, 256, 8, 32),      # P = 2048: one launch, 8-wave send
+    (257, 256, 8, 32),      # P = 2056: one launch, 16-wave send, ragged last block
+    (512, 512, 8, 64),      # P = 4096 at the 16-wave send's largest E
+    (300, 1024, 8, 8),      # E > 512: one launch, 8-wave send in two steps
+    (513, 256, 8, 32),      # P = 4104: separate launches
+    (2049, 8, 2, 8),        # T above the one-wave-per-token routing
+    (3000, 64, 1, 4),
+])
+def test_route_dispatch_shapes(T, E, k, R):
+    m = _m()
+    print(f"[route_dispatch] T={T} E={E} k={k} R={R}", flush=True)
+    lg, xb = _inputs(T, E, 64, T * 7 + E)
+    logits, x = dev_f32(lg), dev_bf16(xb)
+    got = m.moe_route_dispatch(logits, x, k, R)
+    ref = _separate(m, logits, x, k, E, R)
+    torch.cuda.synchronize()
+    _same(got, ref)
+    r_idx, _, _ = oracle.route_topk(lg, k)
+    assert np.array_equal(host(got[0]), r_idx)
+
+
+def test_arrival_counter_returns_to_zero_across_calls():
+    """One workspace reused by calls of varying size (one launch and
+    separate launches) on one stream: each call matches the separate calls
+    and the counter is zero after each."""
+    m = _m()
+    E, k, R, H = 256, 8, 32, 64
+    wsb = m.moe_route_dispatch_workspace_bytes(4096, E, k)
+    ws = torch.zeros((wsb,), dtype=torch.uint8, device=DEV)
+    for i, T in enumerate([128, 300, 64, 4096, 1, 511, 2000, 200]):
+        lg, xb = _inputs(T, E, H, 100 + i)
+        logits, x = dev_f32(lg), dev_bf16(xb)
+        got = m.moe_route_dispatch(logits, x, k, R, workspace=ws)
+        ref = _separate(m, logits, x, k, E, R)
+        torch.cuda.synchronize()
+        _same(got, ref)
+        assert int(ws[:4].view(torch.int32).item()) == 0, T
+
+
+def test_route_dispatch_graph_replays():
+    """The call captured once into a HIP graph and replayed three times, with
+    eager work and a synchronisation between replays: every replay equals
+    the eager result."""
+    m = _m()
+    T, E, k, R, H = 200, 256, 8, 32, 128
+    lg, xb = _inputs(T, E, H, 5)
+    logits, x = dev_f32(lg), dev_bf16(xb)
+    bufs = m.MoeBuffers(T, H, E, k, R)
+    eager = [t.clone() for t in (bufs.route_dispatch(logits, x)[0], bufs.buf[: T * k])]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bufs.route_dispatch(logits, x)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bufs.route_dispatch(logits, x)
+    for _ in range(3):
+        bufs.topk_idx.fill_(-1)
+        bufs.buf.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bufs.topk_idx[:T], eager[0])
+        assert torch.equal(bufs.buf[: T * k].view(torch.int16), eager[1].view(torch.int16))
+        assert int(bufs.route_workspace[:4].view(torch.int32).item()) == 0
