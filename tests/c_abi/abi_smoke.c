@@ -40,6 +40,9 @@ static void host_checks(void) {
   CHECK(moe_dispatch_recv(p16, p16, 16, 256, 2, p16, 31, NULL) == MOE_ERR_CAPACITY);
   CHECK(moe_combine(p16, p16, p16, 16, 256, 33, 1024, p16, NULL) == MOE_ERR_INVALID_ARG);
   CHECK(moe_dispatch_workspace_bytes(8192, 256, 8) > 0);
+  CHECK(moe_route_dispatch_workspace_bytes(128, 256, 8) == 256);
+  CHECK(moe_route_dispatch(p16, p16, 16, 8, 2, 256, 1, p16, p16, p16, p16, p16, p16, NULL, p16, 32,
+                           NULL, 0, NULL) == MOE_ERR_WORKSPACE);
 }
 
 static uint16_t bf16_of(float f) { /* round to nearest even */
@@ -103,6 +106,46 @@ static void gpu_checks(void) {
   HIPCHECK(hipMemcpy(rt, d_rt, sizeof(int32_t) * P, hipMemcpyDeviceToHost));
   HIPCHECK(hipMemcpy(buf, d_buf, 2 * (size_t)P * H, hipMemcpyDeviceToHost));
   HIPCHECK(hipMemcpy(out, d_out, 2 * T * H, hipMemcpyDeviceToHost));
+
+  /* moe_route_dispatch (route and send in one launch at this size) into
+     fresh buffers: the same bytes as the three separate calls. */
+  {
+    float* d_w2;
+    int32_t *d_idx2, *d_counts2, *d_off2, *d_pr2, *d_rt2, *d_roff2;
+    void *d_buf2, *d_ws2;
+    const size_t rwsb = moe_route_dispatch_workspace_bytes(T, E, K);
+    HIPCHECK(hipMalloc((void**)&d_w2, sizeof(float) * P));
+    HIPCHECK(hipMalloc((void**)&d_idx2, sizeof(int32_t) * P));
+    HIPCHECK(hipMalloc((void**)&d_counts2, sizeof(int32_t) * E));
+    HIPCHECK(hipMalloc((void**)&d_off2, sizeof(int32_t) * (E + 1)));
+    HIPCHECK(hipMalloc((void**)&d_pr2, sizeof(int32_t) * P));
+    HIPCHECK(hipMalloc((void**)&d_rt2, sizeof(int32_t) * P));
+    HIPCHECK(hipMalloc((void**)&d_roff2, sizeof(int32_t) * (R + 1)));
+    HIPCHECK(hipMalloc(&d_buf2, 2 * (size_t)P * H));
+    HIPCHECK(hipMalloc(&d_ws2, rwsb));
+    HIPCHECK(hipMemset(d_ws2, 0, rwsb)); /* the arrival counter starts at zero */
+    for (int rep = 0; rep < 2; ++rep)
+      CHECK(moe_route_dispatch(d_logits, d_x, T, E, K, H, R, d_idx2, d_w2, d_counts2, d_off2,
+                               d_pr2, d_rt2, d_roff2, d_buf2, P, d_ws2, rwsb, NULL) == MOE_OK);
+    HIPCHECK(hipDeviceSynchronize());
+    int32_t* i2 = malloc(sizeof(int32_t) * P);
+    int32_t* r2 = malloc(sizeof(int32_t) * P);
+    uint16_t* b2 = malloc(2 * (size_t)P * H);
+    uint32_t counter = 1;
+    HIPCHECK(hipMemcpy(i2, d_idx2, sizeof(int32_t) * P, hipMemcpyDeviceToHost));
+    CHECK(memcmp(i2, idx, sizeof(int32_t) * P) == 0);
+    HIPCHECK(hipMemcpy(i2, d_pr2, sizeof(int32_t) * P, hipMemcpyDeviceToHost));
+    CHECK(memcmp(i2, pr, sizeof(int32_t) * P) == 0);
+    HIPCHECK(hipMemcpy(r2, d_rt2, sizeof(int32_t) * P, hipMemcpyDeviceToHost));
+    CHECK(memcmp(r2, rt, sizeof(int32_t) * P) == 0);
+    HIPCHECK(hipMemcpy(b2, d_buf2, 2 * (size_t)P * H, hipMemcpyDeviceToHost));
+    CHECK(memcmp(b2, buf, 2 * (size_t)P * H) == 0);
+    HIPCHECK(hipMemcpy(&counter, d_ws2, sizeof(counter), hipMemcpyDeviceToHost));
+    CHECK(counter == 0);
+    free(i2); free(r2); free(b2);
+    hipFree(d_w2); hipFree(d_idx2); hipFree(d_counts2); hipFree(d_off2); hipFree(d_pr2);
+    hipFree(d_rt2); hipFree(d_roff2); hipFree(d_buf2); hipFree(d_ws2);
+  }
 
   long total = 0;
   for (int e = 0; e < E; ++e) {
