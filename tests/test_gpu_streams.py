@@ -61,3 +61,37 @@ def test_row_kernels_loop_when_units_exceed_one_launch():
     assert np.array_equal(hb, expect)
     # k = 1 with weight 1: out = x except -0 -> +0
     assert np.array_equal(host_bf16(out), np.where(x == 0x8000, np.uint16(0), x))
+
+
+def test_route_dispatch_on_two_streams_at_once():
+    """Two batches through moe_route_dispatch on two streams at the same time,
+    each with its own workspace (small batches: one route + send launch each,
+    so two arrival counters are live together): both match the oracle, and
+    both counters are back at zero."""
+    import combine_topk_route_amd as m
+
+    print("[streams] route_dispatch, two streams", flush=True)
+    E, k, R, H = 256, 8, 32, 256
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    cases = []
+    for i, T in enumerate((200, 333)):
+        rng = np.random.default_rng(40 + i)
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+        xb = workloads.bf16_from_f32(rng.standard_normal((T, H)).astype(np.float32))
+        ws = torch.zeros((m.moe_route_dispatch_workspace_bytes(T, E, k),), dtype=torch.uint8,
+                         device="cuda")
+        cases.append((lg, xb, dev_f32(lg), dev_bf16(xb), ws))
+    torch.cuda.synchronize()
+    results = []
+    for rep in range(3):
+        for (lg, xb, logits, x, ws), st in zip(cases, streams):
+            results.append(m.moe_route_dispatch(logits, x, k, R, workspace=ws, stream=st))
+    torch.cuda.synchronize()
+    for i, (lg, xb, logits, x, ws) in enumerate(cases):
+        idx, w, send, buf = results[-2 + i]
+        r_idx, _, _ = oracle.route_topk(lg, k)
+        pr, rt = oracle.dispatch_slots(r_idx, E)
+        assert np.array_equal(host(idx), r_idx)
+        assert np.array_equal(host(send.pair_row), pr)
+        assert np.array_equal(host_bf16(buf), xb[rt])
+        assert int(ws[:4].view(torch.int32).item()) == 0
