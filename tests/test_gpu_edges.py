@@ -81,6 +81,25 @@ def test_route_lane_group_shapes(T, E, k):
     _route_check(logits, k)
 
 
+@pytest.mark.parametrize("T,E,k", [
+    (16384, 256, 8),     # 16 lanes per token, 16 experts per lane, 16-byte loads
+    (16390, 384, 8),     # 16 lanes, 24 experts per lane, ragged last wave
+    (8200, 512, 8),      # 32 lanes, 16 experts per lane
+    (8200, 640, 6),      # 32 lanes, 24 per lane (20 used)
+    (16400, 130, 4),     # 16 lanes, 16 per lane (9 used), scalar loads (E % 4 != 0)
+    (16384, 200, 17),    # k > 16: 32 lanes, lane g < k reports winner g
+])
+def test_route_large_batches(T, E, k):
+    """Batch sizes at which the routing kernel uses its fewest lanes per
+    token (16 or 32) and most experts per lane, with Zipf-skewed logits so
+    that winners crowd into a few lanes."""
+    rng = np.random.default_rng(T + E + k)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits += np.log(np.arange(1, E + 1, dtype=np.float64) ** -1.1)[rng.permutation(E)].astype(
+        np.float32)
+    _route_check(logits, k)
+
+
 def test_route_winners_crowded_into_one_lane():
     """Many winners held by one lane of a token (consecutive experts), with
     ties among them: the lane's cache of best candidates empties and is
