@@ -10,8 +10,9 @@
 // H200; here everything is one GPU, and the kernels are shaped for wave64,
 // DPP/ballot cross-lane operations, LDS and HBM3E:
 //
-//   route_topk_kernel    16 lanes per token (32 or 64 for E > 384 or k > 16),
-//                        each holding consecutive experts: fp32 softmax over
+//   route_topk_kernel    batches above 2048 tokens: 16, 32 or 64 lanes per
+//                        token (the fewest that still fill the chip), each
+//                        lane holding consecutive experts: fp32 softmax over
 //                        the E logits held in registers; every lane caches
 //                        its 4 best order-preserving 32-bit keys, so each of
 //                        the k selection rounds is one DPP maximum over the
@@ -29,6 +30,10 @@
 //                        which every block scans for itself.  Small inputs run
 //                        histogram, scan and slots in one block of 8 or 16
 //                        waves.
+//   route_send_kernel    small batches: routing (one wave per token) and the
+//                        single-block send in one launch; the last block to
+//                        finish routing, found with a device-scope arrival
+//                        counter, runs the send.
 //   dispatch_recv_kernel one block per (token, 1 KiB column slice); each wave
 //                        copies the slice to one of the token's k rows: a
 //                        cached 16-byte load (the block's waves share it) and
