@@ -79,19 +79,23 @@ def cpu_baseline(cfg_name: str, sample_tokens: int, seed: int) -> dict:
     cfg = wl.cfg
     t0 = time.perf_counter()
     idx, _, w32 = oracle.route_topk(wl.logits, cfg.k)
+    t1 = time.perf_counter()
     counts = oracle.expert_counts(idx, cfg.E)
     oracle.expert_offsets(counts)
     pr, _ = oracle.dispatch_slots(idx, cfg.E)
     oracle.dispatch_rows(wl.x, pr, sample_tokens * cfg.k)
+    t2 = time.perf_counter()
     oracle.combine(wl.y, pr, w32)
-    dt = time.perf_counter() - t0
+    t3 = time.perf_counter()
+    dt = t3 - t0
     return {
         "value": sample_tokens / dt,
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
         "sample": (f"first {sample_tokens} of {cfg.T} tokens of {cfg_name} (same seed and "
-                   f"distribution), route+dispatch+combine in numpy, {dt:.1f} s, "
+                   f"distribution), route+dispatch+combine in numpy, {dt:.1f} s (route "
+                   f"{t1 - t0:.1f} s, dispatch {t2 - t1:.1f} s, combine {t3 - t2:.1f} s), "
                    f"host has {os.cpu_count()} cpus, affinity {len(os.sched_getaffinity(0))}"),
     }
 
