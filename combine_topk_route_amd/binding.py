@@ -247,11 +247,13 @@ def moe_route_dispatch_workspace_bytes(T: int, E: int, k: int) -> int:
 
 
 def moe_route_dispatch(logits: torch.Tensor, x: torch.Tensor, k: int, num_vranks: int = 1, *,
-                       topk_idx=None, topk_w=None, buf=None, capacity=None, expert_counts=None,
-                       expert_offsets=None, pair_row=None, row_token=None, rank_offsets=None,
+                       n_group: int = 1, topk_group: int = 1, topk_idx=None, topk_w=None,
+                       buf=None, capacity=None, expert_counts=None, expert_offsets=None,
+                       pair_row=None, row_token=None, rank_offsets=None,
                        with_rank_offsets: bool = True, workspace=None, stream=None):
     """Route, send and receive in one call; returns (topk_idx, topk_w,
-    SendResult, buf).  ``workspace`` (uint8, at least
+    SendResult, buf).  ``n_group`` / ``topk_group`` select group-limited
+    routing as in moe_route_topk_grouped.  ``workspace`` (uint8, at least
     moe_route_dispatch_workspace_bytes bytes) must start zeroed the first time
     it is used; it is allocated zeroed here when not given.  Keep one
     workspace per stream and do not pass it to the other dispatch calls."""
@@ -284,7 +286,7 @@ def moe_route_dispatch(logits: torch.Tensor, x: torch.Tensor, k: int, num_vranks
     wsp = _dev(workspace, "workspace", torch.uint8, device=d)
     cp, op, pp, tp, rp = _send_ptrs(out, d)
     _check("moe_route_dispatch", _lib.load().moe_route_dispatch(
-        lp, xp, T, E, k, H, num_vranks, ip, wp, cp, op, pp, tp, rp,
+        lp, xp, T, E, k, n_group, topk_group, H, num_vranks, ip, wp, cp, op, pp, tp, rp,
         _dev(buf, "buf", torch.bfloat16, device=d), capacity, wsp, workspace.numel(),
         _stream(stream, logits)))
     return topk_idx, topk_w, out, buf

@@ -80,12 +80,14 @@ class MoeBuffers:
                         workspace=self.workspace, stream=stream)
         return s, self.buf[: T * self.k]
 
-    def route_dispatch(self, logits: torch.Tensor, x: torch.Tensor, stream=None):
+    def route_dispatch(self, logits: torch.Tensor, x: torch.Tensor, n_group: int = 1,
+                       topk_group: int = 1, stream=None):
         """Route + send + receive in one call; returns (topk_idx, topk_w,
         SendResult, buf [T*k, H])."""
         T = self._t(x.shape[0])
         s = self._send(T)
-        _b.moe_route_dispatch(logits, x, self.k, self.R, topk_idx=self.topk_idx[:T],
+        _b.moe_route_dispatch(logits, x, self.k, self.R, n_group=n_group, topk_group=topk_group,
+                              topk_idx=self.topk_idx[:T],
                               topk_w=self.topk_w[:T], buf=self.buf[: T * self.k],
                               expert_counts=s.expert_counts, expert_offsets=s.expert_offsets,
                               pair_row=s.pair_row, row_token=s.row_token,

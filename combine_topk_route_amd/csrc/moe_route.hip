@@ -881,17 +881,18 @@ __global__ __launch_bounds__(THREADS) void send_rank_kernel(
 // sees every token's routing and runs the single-block send; it then resets
 // the counter for the next call on the stream.  No block ever waits for
 // another, so the grid drains whatever the residency.
-template <int IPL, int THREADS>
+template <int IPL, int THREADS, bool GROUPED>
 __global__ __launch_bounds__(THREADS) void route_send_kernel(
-    const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, uint32_t* __restrict__ arrivals, int nbits, int L, int R,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    const float* __restrict__ logits, int64_t T, int E, int k, int n_group, int topk_group,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, uint32_t* __restrict__ arrivals,
+    int nbits, int L, int R, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ rank_offsets, int32_t* __restrict__ pair_row,
     int32_t* __restrict__ row_token) {
   extern __shared__ int32_t sm[];
   __shared__ int32_t is_last;
   const int64_t t = int64_t(blockIdx.x) * (THREADS / kWave) + threadIdx.x / kWave;
-  if (t < T) route_wave_token<IPL, false>(logits, t, E, k, 1, 1, topk_idx, topk_w);
+  if (t < T)
+    route_wave_token<IPL, GROUPED>(logits, t, E, k, n_group, topk_group, topk_idx, topk_w);
   // Release the block's routing at device scope before it counts in: each
   // wave for its own stores, then thread 0 for all that the barrier ordered
   // before it.  The last block to arrive acquires, so it sees every block's
@@ -1275,6 +1276,13 @@ int enqueue_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t 
   return MOE_ERR_INVALID_ARG;  // unreachable: plan_route covers every E <= 1024, k <= 32
 }
 
+int check_groups(int32_t E, int32_t k, int32_t n_group, int32_t topk_group) {
+  if (n_group < 1 || n_group > kMaxGroups || E % n_group != 0) return MOE_ERR_INVALID_ARG;
+  if (topk_group < 1 || topk_group > n_group || int64_t(topk_group) * (E / n_group) < k)
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
 int check_rows(int64_t T, int32_t H, int32_t k, int64_t capacity, const void* rows_in,
                const void* rows_out) {
   if (T < 0 || k < 1 || k > kMaxK || T > kMaxPairs / k) return MOE_ERR_INVALID_ARG;
@@ -1382,10 +1390,11 @@ bool route_send_fusable(int64_t T, int32_t E, int32_t k) {
   return T <= kRouteWaveMaxTokens && plan_send(T * k, E).fused;
 }
 
-int enqueue_route_send(const float* logits, int64_t T, int32_t E, int32_t k, int32_t R,
-                       int32_t* topk_idx, float* topk_w, uint32_t* arrivals, int32_t* counts,
-                       int32_t* offsets, int32_t* pair_row, int32_t* row_token,
-                       int32_t* rank_offsets, hipStream_t st) {
+int enqueue_route_send(const float* logits, int64_t T, int32_t E, int32_t k, int32_t n_group,
+                       int32_t topk_group, int32_t R, int32_t* topk_idx, float* topk_w,
+                       uint32_t* arrivals, int32_t* counts, int32_t* offsets, int32_t* pair_row,
+                       int32_t* row_token, int32_t* rank_offsets, hipStream_t st) {
+  const bool grouped = topk_group < n_group;  // keeping every group is plain top-k
   const SendPlan plan = plan_send(T * k, E);
   const int waves = plan.threads / kWave;
   const size_t lds = (size_t(waves) * E + E + 17) * sizeof(int32_t);
@@ -1393,10 +1402,13 @@ int enqueue_route_send(const float* logits, int64_t T, int32_t E, int32_t k, int
   const int ipl = (E + kWave - 1) / kWave;
   const int nbits = nbits_for(E);
   const int L = E / R;
-#define MOE_FUSED(IPL_, THR_)                                                                  \
-  return launch(route_send_kernel<IPL_, THR_>, grid, dim3(THR_), lds, st, logits, T, E, k,     \
-                topk_idx, topk_w, arrivals, nbits, L, R, counts, offsets, rank_offsets,        \
-                pair_row, row_token)
+#define MOE_FUSED(IPL_, THR_)                                                                 \
+  return grouped ? launch(route_send_kernel<IPL_, THR_, true>, grid, dim3(THR_), lds, st,     \
+                          logits, T, E, k, n_group, topk_group, topk_idx, topk_w, arrivals,   \
+                          nbits, L, R, counts, offsets, rank_offsets, pair_row, row_token)    \
+                 : launch(route_send_kernel<IPL_, THR_, false>, grid, dim3(THR_), lds, st,    \
+                          logits, T, E, k, 1, 1, topk_idx, topk_w, arrivals, nbits, L, R,     \
+                          counts, offsets, rank_offsets, pair_row, row_token)
 #define MOE_FUSED_IPL(THR_)        \
   if (ipl <= 1) MOE_FUSED(1, THR_); \
   if (ipl <= 2) MOE_FUSED(2, THR_); \
@@ -1436,11 +1448,10 @@ int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t
 
 int moe_route_topk_grouped(const float* logits, int64_t T, int32_t E, int32_t k, int32_t n_group,
                            int32_t topk_group, int32_t* topk_idx, float* topk_w, void* stream) {
-  const int st = check_route_shape(T, E, k);
+  int st = check_route_shape(T, E, k);
   if (st != MOE_OK) return st;
-  if (n_group < 1 || n_group > kMaxGroups || E % n_group != 0) return MOE_ERR_INVALID_ARG;
-  if (topk_group < 1 || topk_group > n_group || int64_t(topk_group) * (E / n_group) < k)
-    return MOE_ERR_INVALID_ARG;
+  st = check_groups(E, k, n_group, topk_group);
+  if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
   if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_ERR_ALIGNMENT;
@@ -1495,11 +1506,14 @@ size_t moe_route_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k) {
 }
 
 int moe_route_dispatch(const float* logits, const void* x, int64_t T, int32_t E, int32_t k,
-                       int32_t H, int32_t num_vranks, int32_t* topk_idx, float* topk_w,
-                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* pair_row,
-                       int32_t* row_token, int32_t* rank_offsets, void* buf, int64_t capacity,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       int32_t n_group, int32_t topk_group, int32_t H, int32_t num_vranks,
+                       int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
+                       int32_t* expert_offsets, int32_t* pair_row, int32_t* row_token,
+                       int32_t* rank_offsets, void* buf, int64_t capacity, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   int st = check_route_shape(T, E, k);
+  if (st != MOE_OK) return st;
+  st = check_groups(E, k, n_group, topk_group);
   if (st != MOE_OK) return st;
   if (T > 0 && (!logits || !topk_idx || !topk_w)) return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)))
@@ -1515,11 +1529,11 @@ int moe_route_dispatch(const float* logits, const void* x, int64_t T, int32_t E,
   if (!aligned(workspace, 4)) return MOE_ERR_ALIGNMENT;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (route_send_fusable(T, E, k)) {
-    st = enqueue_route_send(logits, T, E, k, num_vranks, topk_idx, topk_w,
+    st = enqueue_route_send(logits, T, E, k, n_group, topk_group, num_vranks, topk_idx, topk_w,
                             static_cast<uint32_t*>(workspace), expert_counts, expert_offsets,
                             pair_row, row_token, rank_offsets, s);
   } else {
-    st = enqueue_route(logits, T, E, k, 1, 1, topk_idx, topk_w, s);
+    st = enqueue_route(logits, T, E, k, n_group, topk_group, topk_idx, topk_w, s);
     if (st == MOE_OK)
       st = enqueue_send(topk_idx, T, E, k, num_vranks, expert_counts, expert_offsets, pair_row,
                         row_token, rank_offsets, ws + kArrivalBytes, s);

@@ -195,8 +195,10 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int64_t T, int32_t E,
  * communication", sections "Introduction" and "Dispatch"; "Lower latency and
  * higher throughput with multi-node DeepSeek deployment", section "MoE
  * Router").  Arguments are the union of the three calls', with the same
- * meaning; topk_idx and topk_w are outputs.  All are checked before anything
- * is enqueued.  The outputs are identical to the three separate calls.
+ * meaning; topk_idx and topk_w are outputs.  n_group and topk_group select
+ * group-limited routing as in moe_route_topk_grouped (n_group = topk_group =
+ * 1 is plain moe_route_topk).  All arguments are checked before anything is
+ * enqueued.  The outputs are identical to the separate calls.
  *
  * Small batches (T <= 2048 and T*k <= 4096) route and send in one launch:
  * the last routing block to finish runs the single-block send, found with an
@@ -213,7 +215,8 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int64_t T, int32_t E,
  *         workspace (T > 0).
  */
 int moe_route_dispatch(const float* logits, const void* x, int64_t T, int32_t E,
-                       int32_t k, int32_t H, int32_t num_vranks,
+                       int32_t k, int32_t n_group, int32_t topk_group,
+                       int32_t H, int32_t num_vranks,
                        int32_t* topk_idx, float* topk_w,
                        int32_t* expert_counts, int32_t* expert_offsets,
                        int32_t* pair_row, int32_t* row_token, int32_t* rank_offsets,

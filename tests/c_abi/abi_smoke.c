@@ -41,8 +41,10 @@ static void host_checks(void) {
   CHECK(moe_combine(p16, p16, p16, 16, 256, 33, 1024, p16, NULL) == MOE_ERR_INVALID_ARG);
   CHECK(moe_dispatch_workspace_bytes(8192, 256, 8) > 0);
   CHECK(moe_route_dispatch_workspace_bytes(128, 256, 8) == 256);
-  CHECK(moe_route_dispatch(p16, p16, 16, 8, 2, 256, 1, p16, p16, p16, p16, p16, p16, NULL, p16, 32,
-                           NULL, 0, NULL) == MOE_ERR_WORKSPACE);
+  CHECK(moe_route_dispatch(p16, p16, 16, 8, 2, 1, 1, 256, 1, p16, p16, p16, p16, p16, p16, NULL, p16,
+                           32, NULL, 0, NULL) == MOE_ERR_WORKSPACE);
+  CHECK(moe_route_dispatch(p16, p16, 16, 8, 2, 3, 1, 256, 1, p16, p16, p16, p16, p16, p16, NULL, p16,
+                           32, p16, 256, NULL) == MOE_ERR_INVALID_ARG); /* E % n_group != 0 */
 }
 
 static uint16_t bf16_of(float f) { /* round to nearest even */
@@ -125,7 +127,7 @@ static void gpu_checks(void) {
     HIPCHECK(hipMalloc(&d_ws2, rwsb));
     HIPCHECK(hipMemset(d_ws2, 0, rwsb)); /* the arrival counter starts at zero */
     for (int rep = 0; rep < 2; ++rep)
-      CHECK(moe_route_dispatch(d_logits, d_x, T, E, K, H, R, d_idx2, d_w2, d_counts2, d_off2,
+      CHECK(moe_route_dispatch(d_logits, d_x, T, E, K, 1, 1, H, R, d_idx2, d_w2, d_counts2, d_off2,
                                d_pr2, d_rt2, d_roff2, d_buf2, P, d_ws2, rwsb, NULL) == MOE_OK);
     HIPCHECK(hipDeviceSynchronize());
     int32_t* i2 = malloc(sizeof(int32_t) * P);

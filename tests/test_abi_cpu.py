@@ -203,9 +203,10 @@ def test_route_dispatch_checks_every_part_before_enqueueing(lib):
     assert wsf(8192, 256, 8) == 256 + lib.moe_dispatch_workspace_bytes(8192, 256, 8)
     assert wsf(8192, 0, 8) == 0
     ws = wsf(8192, 256, 8)
-    # logits, x, T, E, k, H, R, idx, w, counts, offsets, pair_row, row_token, rank, buf, cap, ws, wsb
-    base = [P16, P16, 8192, 256, 8, 7168, 32, P16, P16, P16, P16, P16, P16, None, P16, 8192 * 8,
-            P16, ws, S]
+    # logits, x, T, E, k, n_group, topk_group, H, R, idx, w, counts, offsets, pair_row,
+    # row_token, rank, buf, cap, ws, wsb
+    base = [P16, P16, 8192, 256, 8, 1, 1, 7168, 32, P16, P16, P16, P16, P16, P16, None, P16,
+            8192 * 8, P16, ws, S]
 
     def call(**kw):
         a = list(base)
@@ -214,15 +215,18 @@ def test_route_dispatch_checks_every_part_before_enqueueing(lib):
         return f(*a)
 
     assert call(a4=33) == INVALID                  # k > 32 (routing)
-    assert call(a0=None) == INVALID               # null logits
-    assert call(a8=None) == INVALID               # null weights
-    assert call(a0=P16 + 2) == ALIGN              # misaligned logits
-    assert call(a6=5) == INVALID                  # E % R != 0 (send)
-    assert call(a15=8192 * 8 - 1) == CAP          # capacity < T*k (recv)
-    assert call(a5=7170) == ALIGN                 # H % 8 != 0
-    assert call(a16=None) == WS                   # no workspace
-    assert call(a17=ws - 1) == WS                 # short: the send part does not fit
-    assert call(a2=128, a15=1024, a17=255) == WS  # short: no room for the counter
-    assert call(a2=128, a15=1024, a17=256, a16=P16 + 2) == ALIGN
-    assert call(a2=0, a0=None, a1=None, a7=None, a8=None, a9=None, a10=None, a11=None, a12=None,
-                a14=None, a15=0, a16=None, a17=0) == OK
+    assert call(a5=3) == INVALID                   # E % n_group != 0
+    assert call(a5=8, a6=9) == INVALID             # topk_group > n_group
+    assert call(a5=64, a6=1) == INVALID            # one group of 4 experts < k
+    assert call(a0=None) == INVALID                # null logits
+    assert call(a10=None) == INVALID               # null weights
+    assert call(a0=P16 + 2) == ALIGN               # misaligned logits
+    assert call(a8=5) == INVALID                   # E % R != 0 (send)
+    assert call(a17=8192 * 8 - 1) == CAP           # capacity < T*k (recv)
+    assert call(a7=7170) == ALIGN                  # H % 8 != 0
+    assert call(a18=None) == WS                    # no workspace
+    assert call(a19=ws - 1) == WS                  # short: the send part does not fit
+    assert call(a2=128, a17=1024, a19=255) == WS   # short: no room for the counter
+    assert call(a2=128, a17=1024, a19=256, a18=P16 + 2) == ALIGN
+    assert call(a2=0, a0=None, a1=None, a9=None, a10=None, a11=None, a12=None, a13=None,
+                a14=None, a16=None, a17=0, a18=None, a19=0) == OK

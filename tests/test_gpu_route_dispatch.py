@@ -132,3 +132,23 @@ def test_route_dispatch_graph_replays():
         assert torch.equal(bufs.topk_idx[:T], eager[0])
         assert torch.equal(bufs.buf[: T * k].view(torch.int16), eager[1].view(torch.int16))
         assert int(bufs.route_workspace[:4].view(torch.int32).item()) == 0
+
+
+@pytest.mark.parametrize("T,E,k,G,TG,R", [
+    (128, 256, 8, 8, 4, 32),     # DeepSeek-V3 shape, decode-sized: one launch
+    (300, 384, 8, 8, 4, 48),     # 16-wave single-block send in the same launch
+    (4096, 256, 8, 8, 4, 32),    # separate launches
+    (77, 384, 8, 48, 6, 48),     # many small groups
+])
+def test_grouped_route_dispatch_matches_separate_calls(T, E, k, G, TG, R):
+    m = _m()
+    print(f"[route_dispatch] grouped T={T} E={E} k={k} groups {TG}/{G}", flush=True)
+    lg, xb = _inputs(T, E, 64, T + 11 * E)
+    logits, x = dev_f32(lg), dev_bf16(xb)
+    got = m.moe_route_dispatch(logits, x, k, R, n_group=G, topk_group=TG)
+    idx, w = m.moe_route_topk_grouped(logits, k, G, TG)
+    send, buf = m.moe_dispatch(idx, x, E, R)
+    torch.cuda.synchronize()
+    _same(got, (idx, w, send, buf))
+    r_idx, _, _ = oracle.route_topk_grouped(lg, k, G, TG)
+    assert np.array_equal(host(got[0]), r_idx)
