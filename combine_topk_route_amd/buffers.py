@@ -52,19 +52,28 @@ class MoeBuffers:
         if fp8:
             self.buf_q = torch.empty((cap, hidden), dtype=torch.uint8, device=dev)
             self.buf_scale = torch.empty((cap, hidden // 128), dtype=f32, device=dev)
+        self._views = None
 
     def _t(self, T: int) -> int:
         if not 0 <= T <= self.max_tokens:
             raise ValueError(f"batch of {T} tokens exceeds max_tokens={self.max_tokens}")
         return T
 
+    def _v(self, T: int) -> "_Views":
+        """The buffers' views for a batch of T tokens, kept for the most recent
+        T: slicing a tensor costs about a microsecond of host time, as much as
+        a decode-sized kernel."""
+        v = self._views
+        if v is None or v.T != T:
+            v = self._views = _Views(self, self._t(T))
+        return v
+
     def _send(self, T):
-        return _b.SendResult(self.expert_counts, self.expert_offsets, self.pair_row[:T],
-                             self.row_token[: T * self.k], self.rank_offsets)
+        return self._v(T).send
 
     def route(self, logits: torch.Tensor, n_group: int = 1, topk_group: int = 1, stream=None):
-        T = self._t(logits.shape[0])
-        idx, w = self.topk_idx[:T], self.topk_w[:T]
+        v = self._v(logits.shape[0])
+        idx, w = v.topk_idx, v.topk_w
         if n_group == 1:
             return _b.moe_route_topk(logits, self.k, topk_idx=idx, topk_w=w, stream=stream)
         return _b.moe_route_topk_grouped(logits, self.k, n_group, topk_group, topk_idx=idx,
@@ -72,28 +81,27 @@ class MoeBuffers:
 
     def dispatch(self, topk_idx: torch.Tensor, x: torch.Tensor, stream=None):
         """Send + receive; returns (SendResult, buf [T*k, H])."""
-        T = self._t(x.shape[0])
-        s = self._send(T)
-        _b.moe_dispatch(topk_idx, x, self.E, self.R, buf=self.buf[: T * self.k],
+        v = self._v(x.shape[0])
+        s = v.send
+        _b.moe_dispatch(topk_idx, x, self.E, self.R, buf=v.buf,
                         expert_counts=s.expert_counts, expert_offsets=s.expert_offsets,
                         pair_row=s.pair_row, row_token=s.row_token, rank_offsets=s.rank_offsets,
                         workspace=self.workspace, stream=stream)
-        return s, self.buf[: T * self.k]
+        return s, v.buf
 
     def route_dispatch(self, logits: torch.Tensor, x: torch.Tensor, n_group: int = 1,
                        topk_group: int = 1, stream=None):
         """Route + send + receive in one call; returns (topk_idx, topk_w,
         SendResult, buf [T*k, H])."""
-        T = self._t(x.shape[0])
-        s = self._send(T)
+        v = self._v(x.shape[0])
+        s = v.send
         _b.moe_route_dispatch(logits, x, self.k, self.R, n_group=n_group, topk_group=topk_group,
-                              topk_idx=self.topk_idx[:T],
-                              topk_w=self.topk_w[:T], buf=self.buf[: T * self.k],
+                              topk_idx=v.topk_idx, topk_w=v.topk_w, buf=v.buf,
                               expert_counts=s.expert_counts, expert_offsets=s.expert_offsets,
                               pair_row=s.pair_row, row_token=s.row_token,
                               rank_offsets=s.rank_offsets, workspace=self.route_workspace,
                               stream=stream)
-        return self.topk_idx[:T], self.topk_w[:T], s, self.buf[: T * self.k]
+        return v.topk_idx, v.topk_w, s, v.buf
 
     def dispatch_fp8(self, topk_idx: torch.Tensor, x: torch.Tensor, stream=None):
         """Send + fp8 receive; returns (SendResult, codes [T*k, H], scales [T*k, H/128])."""
@@ -111,5 +119,17 @@ class MoeBuffers:
 
     def combine(self, y: torch.Tensor, pair_row: torch.Tensor, topk_w: torch.Tensor,
                 stream=None) -> torch.Tensor:
-        T = self._t(pair_row.shape[0])
-        return _b.moe_combine(y, pair_row, topk_w, out=self.out[:T], stream=stream)
+        v = self._v(pair_row.shape[0])
+        return _b.moe_combine(y, pair_row, topk_w, out=v.out, stream=stream)
+
+
+class _Views:
+    """MoeBuffers' tensors cut to a batch of T tokens."""
+
+    def __init__(self, b: MoeBuffers, T: int):
+        self.T = T
+        self.topk_idx, self.topk_w = b.topk_idx[:T], b.topk_w[:T]
+        self.buf = b.buf[: T * b.k]
+        self.out = b.out[:T]
+        self.send = _b.SendResult(b.expert_counts, b.expert_offsets, b.pair_row[:T],
+                                  b.row_token[: T * b.k], b.rank_offsets)
