@@ -42,8 +42,8 @@ class MoeBuffers:
         self.row_token = torch.empty((cap,), dtype=i32, device=dev)
         ws = _b.moe_dispatch_workspace_bytes(max_tokens, num_experts, k)
         self.workspace = torch.empty((max(ws, 1),), dtype=torch.uint8, device=dev)
-        # route_dispatch's own workspace: its leading arrival counter starts at
-        # zero and every call leaves it at zero.
+        # route_dispatch's own workspace: it starts zeroed and every call
+        # leaves it zeroed.
         rws = _b.moe_route_dispatch_workspace_bytes(max_tokens, num_experts, k)
         self.route_workspace = torch.zeros((max(rws, 1),), dtype=torch.uint8, device=dev)
         self.buf = torch.empty((cap, hidden), dtype=torch.bfloat16, device=dev)

@@ -16,7 +16,10 @@
 //                        the E logits held in registers; every lane caches
 //                        its 4 best order-preserving 32-bit keys, so each of
 //                        the k selection rounds is one DPP maximum over the
-//                        cache heads of the token's lanes.
+//                        cache heads of the token's lanes.  Inside
+//                        moe_route_dispatch (E >= 128) the routing kernels
+//                        also count each pair into the send histogram with
+//                        an atomic add, in place of send_hist_kernel.
 //   route_wave_kernel    one wave per token (group-limited routing, and plain
 //                        routing of small batches): k rounds of a wave-wide
 //                        maximum of the keys, the lowest expert index holding
@@ -229,6 +232,10 @@ __device__ __forceinline__ float key_value(uint32_t key) {
 constexpr int kRouteWavesPerBlock = 4;
 constexpr int kRouteThreads = kRouteWavesPerBlock * kWave;
 constexpr int64_t kRouteWaveMaxTokens = 2048;  // up to here plain routing uses one wave per token
+// Fewest experts for which moe_route_dispatch's routing kernel counts the send
+// histogram itself: with fewer, its per-pair atomics pile onto too few
+// addresses (E = 8: each takes a few hundred).
+constexpr int kRouteCountMinE = 128;
 
 // Softmax numerator exp(a - m).  The difference is split into its fp32
 // rounding d and the exact remainder r (TwoSum), and exp(d + r) is taken as
@@ -357,10 +364,13 @@ __device__ __forceinline__ void cache_push(uint32_t kv, int i, uint32_t (&h)[C],
 // for the best C after the popped one; with C = 4 that needs a lane to hold
 // four of a token's winners (about 1 % of tokens at E = 256, k = 8).
 // VEC: 16-byte logit loads (IPL % 4 == 0, E % 4 == 0, 16-byte aligned rows).
-template <int G, int IPL, bool VEC>
+// COUNT: the owner of winner j also adds the pair p = t*k + j to the send
+// histogram matrix, row p / chunk (chunk >= 64 > j, so a token's pairs span at
+// most two rows); the matrix must hold zeros beforehand.
+template <int G, int IPL, bool VEC, bool COUNT>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w) {
+    float* __restrict__ topk_w, int32_t* __restrict__ hist_mat, uint32_t chunk) {
   constexpr int TPW = kWave / G;         // tokens per wave
   constexpr int C = IPL < 4 ? IPL : 4;   // cached candidates per lane
   const int lane = lane_id();
@@ -374,6 +384,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
   const int e0 = g * IPL;
   const float* row = logits + t_ld * E + e0;
   int32_t* idx_out = topk_idx + t_ld * k;
+  uint32_t row0 = 0u, rem0 = 0u;  // histogram row and offset in it of the pair t*k
+  if constexpr (COUNT) {
+    const uint32_t p0 = uint32_t(t_ld * k);
+    row0 = p0 / chunk;
+    rem0 = p0 - row0 * chunk;
+  }
 
   float lv[IPL];
   if constexpr (VEC) {
@@ -439,7 +455,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     const uint32_t kp = h[0];
     const int ip = hi[0];
     if (owner) {
-      if (t < T) idx_out[j] = e0 + ip;  // the owner reports winner j
+      if (t < T) {
+        idx_out[j] = e0 + ip;  // the owner reports winner j
+        if constexpr (COUNT) {
+          const uint32_t row = row0 + (rem0 + uint32_t(j) >= chunk ? 1u : 0u);
+          __hip_atomic_fetch_add(hist_mat + size_t(row) * E + e0 + ip, 1, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
       --rem;
 #pragma unroll
       for (int c = 0; c + 1 < C; ++c) {
@@ -485,11 +508,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
 // contiguous groups, a group's score is its largest logit, and only the
 // topk_group best groups (ties to the lower group) take part in the top-k.
 // Routing of token t by the calling wave (all 64 lanes active).
-template <int IPL, bool GROUPED>
+// COUNT: as in route_topk_kernel, lane j < k adds pair t*k + j to the
+// zero-initialised send histogram matrix.
+template <int IPL, bool GROUPED, bool COUNT>
 __device__ __forceinline__ void route_wave_token(const float* __restrict__ logits, int64_t t, int E,
                                                  int k, int n_group, int topk_group,
                                                  int32_t* __restrict__ topk_idx,
-                                                 float* __restrict__ topk_w) {
+                                                 float* __restrict__ topk_w,
+                                                 int32_t* __restrict__ hist_mat, uint32_t chunk) {
   const int lane = lane_id();
   const float* row = logits + t * E;
 
@@ -587,16 +613,23 @@ __device__ __forceinline__ void route_wave_token(const float* __restrict__ logit
     const float psel = (zsum + zcomp) / s;      // their total probability
     topk_idx[t * k + lane] = my_e;
     topk_w[t * k + lane] = p / psel;            // renormalised to sum to 1
+    if constexpr (COUNT) {
+      const uint32_t pr = uint32_t(t * k + lane);
+      __hip_atomic_fetch_add(hist_mat + size_t(pr / chunk) * E + my_e, 1, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
-template <int IPL, bool GROUPED>
+template <int IPL, bool GROUPED, bool COUNT>
 __global__ __launch_bounds__(kRouteThreads) void route_wave_kernel(
     const float* __restrict__ logits, int64_t T, int E, int k, int n_group, int topk_group,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ hist_mat,
+    uint32_t chunk) {
   const int64_t t = int64_t(blockIdx.x) * kRouteWavesPerBlock + threadIdx.x / kWave;
   if (t >= T) return;  // whole waves leave; no block barrier follows
-  route_wave_token<IPL, GROUPED>(logits, t, E, k, n_group, topk_group, topk_idx, topk_w);
+  route_wave_token<IPL, GROUPED, COUNT>(logits, t, E, k, n_group, topk_group, topk_idx, topk_w,
+                                        hist_mat, chunk);
 }
 
 // ---------------------------------------------------------------------------
@@ -702,13 +735,16 @@ __global__ __launch_bounds__(kSendThreads) void send_hist_kernel(const int32_t* 
 // counts themselves (FUSED, one block).  Pass 2 adds the exclusive prefix
 // over waves and the block base, and writes row_token.
 // The rank step of block `bid` (0 for FUSED), run by a block of THREADS
-// threads; sm: its dynamic LDS.
+// threads; sm: its dynamic LDS.  arrivals (multi-block only; nullptr: keep
+// the matrix): each block counts in once it has staged the histogram matrix,
+// and the last one clears the matrix and the counter for the next call.
 template <bool FUSED, int THREADS, int ITEMS>
 __device__ __forceinline__ void send_rank_block(
     int bid, int32_t* sm, const int32_t* __restrict__ idx, int64_t P, int E, int k, int nbits,
-    int64_t chunk, int nb, const int32_t* __restrict__ ws_cnt, int L, int R,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ rank_offsets,
-    int32_t* __restrict__ pair_row, int32_t* __restrict__ row_token) {
+    int64_t chunk, int nb, int32_t* __restrict__ ws_cnt, uint32_t* __restrict__ arrivals, int L,
+    int R, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ pair_row,
+    int32_t* __restrict__ row_token) {
   // LDS: [W][E] per-wave counts | [E] base | [17] scratch | [nb][E] matrix (multi-block)
   constexpr int nwaves = THREADS / kWave;  // launched with THREADS threads (at most 16 waves)
   const int wid = threadIdx.x / kWave;
@@ -747,6 +783,13 @@ __device__ __forceinline__ void send_rank_block(
     }
   }
   __syncthreads();
+  // Every thread's matrix loads have returned (their values are in LDS), so
+  // the block may count in; the result is first needed after pass 1.
+  __shared__ int32_t clear_mat;
+  uint32_t arrived_before = 0u;
+  if (!FUSED && arrivals != nullptr && threadIdx.x == 0)
+    arrived_before =
+        __hip_atomic_fetch_add(arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // Multi-block: totals per expert and this block's prefix.  E <= 2 * blockDim.
   int32_t pre[2] = {0, 0};
@@ -798,6 +841,8 @@ __device__ __forceinline__ void send_rank_block(
       if (!one_step && p < b) pair_row[p] = slot;
     }
   }
+  if (!FUSED && threadIdx.x == 0)
+    clear_mat = arrivals != nullptr && arrived_before == uint32_t(nb - 1);
   __syncthreads();
 
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
@@ -859,17 +904,23 @@ __device__ __forceinline__ void send_rank_block(
       }
     }
   }
+  if (!FUSED && clear_mat) {  // every block has staged the matrix: zero it for the next call
+    for (int i = threadIdx.x; i < nb * E; i += THREADS) ws_cnt[i] = 0;
+    if (threadIdx.x == 0) __hip_atomic_store(arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 template <bool FUSED, int THREADS, int ITEMS>
 __global__ __launch_bounds__(THREADS) void send_rank_kernel(
     const int32_t* __restrict__ idx, int64_t P, int E, int k, int nbits, int64_t chunk, int nb,
-    const int32_t* __restrict__ ws_cnt, int L, int R, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ rank_offsets,
-    int32_t* __restrict__ pair_row, int32_t* __restrict__ row_token) {
+    int32_t* __restrict__ ws_cnt, uint32_t* __restrict__ arrivals, int L, int R,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ pair_row,
+    int32_t* __restrict__ row_token) {
   extern __shared__ int32_t sm[];
   send_rank_block<FUSED, THREADS, ITEMS>(blockIdx.x, sm, idx, P, E, k, nbits, chunk, nb, ws_cnt,
-                                         L, R, counts, offsets, rank_offsets, pair_row, row_token);
+                                         arrivals, L, R, counts, offsets, rank_offsets, pair_row,
+                                         row_token);
 }
 
 // ---------------------------------------------------------------------------
@@ -892,7 +943,8 @@ __global__ __launch_bounds__(THREADS) void route_send_kernel(
   __shared__ int32_t is_last;
   const int64_t t = int64_t(blockIdx.x) * (THREADS / kWave) + threadIdx.x / kWave;
   if (t < T)
-    route_wave_token<IPL, GROUPED>(logits, t, E, k, n_group, topk_group, topk_idx, topk_w);
+    route_wave_token<IPL, GROUPED, false>(logits, t, E, k, n_group, topk_group, topk_idx, topk_w,
+                                          nullptr, 1u);
   // Release the block's routing at device scope before it counts in: each
   // wave for its own stores, then thread 0 for all that the barrier ordered
   // before it.  The last block to arrive acquires, so it sees every block's
@@ -911,8 +963,9 @@ __global__ __launch_bounds__(THREADS) void route_send_kernel(
   if (!is_last) return;  // the whole block leaves
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   const int64_t P = T * k;
-  send_rank_block<true, THREADS, kSendItems>(0, sm, topk_idx, P, E, k, nbits, P, 1, nullptr, L, R,
-                                             counts, offsets, rank_offsets, pair_row, row_token);
+  send_rank_block<true, THREADS, kSendItems>(0, sm, topk_idx, P, E, k, nbits, P, 1, nullptr,
+                                             nullptr, L, R, counts, offsets, rank_offsets,
+                                             pair_row, row_token);
   if (threadIdx.x == 0)  // every block has counted in: ready for the next call on the stream
     __hip_atomic_store(arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1226,35 +1279,51 @@ RoutePlan plan_route(int64_t T, int E, int k) {
   return p;
 }
 
+// hist_mat: nullptr, or the zero-initialised [blocks][E] send histogram
+// matrix with `chunk` pairs per row, which the routing kernels then fill.
 int enqueue_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t n_group,
-                  int32_t topk_group, int32_t* topk_idx, float* topk_w, hipStream_t s) {
+                  int32_t topk_group, int32_t* topk_idx, float* topk_w, hipStream_t s,
+                  int32_t* hist_mat = nullptr, int64_t chunk = 1) {
   const dim3 block(kRouteThreads);
   const bool grouped = topk_group < n_group;  // keeping every group is plain top-k
+  const bool count = hist_mat != nullptr;
+  const uint32_t ch = uint32_t(chunk);
   if (grouped || T <= kRouteWaveMaxTokens) {
     const dim3 grid(unsigned((T + kRouteWavesPerBlock - 1) / kRouteWavesPerBlock));
     const int ipl = (E + kWave - 1) / kWave;
-#define MOE_ROUTE(IPL_)                                                                         \
-  return grouped ? launch(route_wave_kernel<IPL_, true>, grid, block, 0, s, logits, T, E, k,     \
-                          n_group, topk_group, topk_idx, topk_w)                                 \
-                 : launch(route_wave_kernel<IPL_, false>, grid, block, 0, s, logits, T, E, k, 1, \
-                          1, topk_idx, topk_w)
+    const int ng = grouped ? n_group : 1, tg = grouped ? topk_group : 1;
+#define MOE_ROUTE_GC(IPL_, GR_)                                                              \
+  return count ? launch(route_wave_kernel<IPL_, GR_, true>, grid, block, 0, s, logits, T, E, k, \
+                        ng, tg, topk_idx, topk_w, hist_mat, ch)                                \
+               : launch(route_wave_kernel<IPL_, GR_, false>, grid, block, 0, s, logits, T, E, \
+                        k, ng, tg, topk_idx, topk_w, hist_mat, ch)
+#define MOE_ROUTE(IPL_)            \
+  {                                \
+    if (grouped) MOE_ROUTE_GC(IPL_, true); \
+    MOE_ROUTE_GC(IPL_, false);     \
+  }
     if (ipl <= 1) MOE_ROUTE(1);
     if (ipl <= 2) MOE_ROUTE(2);
     if (ipl <= 4) MOE_ROUTE(4);
     if (ipl <= 8) MOE_ROUTE(8);
     MOE_ROUTE(16);
 #undef MOE_ROUTE
+#undef MOE_ROUTE_GC
   }
   const RoutePlan p = plan_route(T, E, k);
   const int64_t tokens_per_block = int64_t(kRouteWavesPerBlock) * (kWave / p.G);
   const dim3 grid(unsigned((T + tokens_per_block - 1) / tokens_per_block));
   const bool vec = p.IPL % 4 == 0 && E % 4 == 0 && aligned(logits, 16);
-#define MOE_ROUTE(G_, IPL_)                                                                     \
-  if (p.G == G_ && p.IPL == IPL_)                                                               \
-    return vec ? launch(route_topk_kernel<G_, IPL_, (IPL_ % 4 == 0)>, grid, block, 0, s, logits, \
-                        T, E, k, topk_idx, topk_w)                                              \
-               : launch(route_topk_kernel<G_, IPL_, false>, grid, block, 0, s, logits, T, E, k, \
-                        topk_idx, topk_w)
+#define MOE_ROUTE_VC(G_, IPL_, VEC_)                                                            \
+  return count ? launch(route_topk_kernel<G_, IPL_, VEC_, true>, grid, block, 0, s, logits, T, \
+                        E, k, topk_idx, topk_w, hist_mat, ch)                                 \
+               : launch(route_topk_kernel<G_, IPL_, VEC_, false>, grid, block, 0, s, logits, T, \
+                        E, k, topk_idx, topk_w, hist_mat, ch)
+#define MOE_ROUTE(G_, IPL_)                      \
+  if (p.G == G_ && p.IPL == IPL_) {              \
+    if (vec) MOE_ROUTE_VC(G_, IPL_, (IPL_ % 4 == 0)); \
+    MOE_ROUTE_VC(G_, IPL_, false);               \
+  }
   MOE_ROUTE(16, 1);
   MOE_ROUTE(16, 2);
   MOE_ROUTE(16, 4);
@@ -1273,6 +1342,7 @@ int enqueue_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t 
   MOE_ROUTE(64, 8);
   MOE_ROUTE(64, 16);
 #undef MOE_ROUTE
+#undef MOE_ROUTE_VC
   return MOE_ERR_INVALID_ARG;  // unreachable: plan_route covers every E <= 1024, k <= 32
 }
 
@@ -1321,6 +1391,28 @@ int check_send(const int32_t* topk_idx, int64_t T, int32_t E, int32_t k, int32_t
   return MOE_OK;
 }
 
+// The histogram kernel of the multi-block send: fills the [blocks][E] matrix.
+int enqueue_send_hist(const int32_t* topk_idx, int64_t T, int32_t E, int32_t k, int32_t* mat,
+                      hipStream_t st) {
+  const SendPlan plan = plan_send(T * k, E);
+  return launch(send_hist_kernel, dim3(plan.nb), dim3(kSendThreads), size_t(E) * 4, st, topk_idx,
+                T * k, E, nbits_for(E), plan.chunk, mat);
+}
+
+// The rank kernel of the multi-block send, given the filled [blocks][E]
+// histogram matrix.
+// histogram matrix, which it zeroes afterwards when `arrivals` is given.
+int enqueue_send_ranks(const int32_t* topk_idx, int64_t T, int32_t E, int32_t k, int32_t R,
+                       int32_t* counts, int32_t* offsets, int32_t* pair_row, int32_t* row_token,
+                       int32_t* rank_offsets, int32_t* mat, uint32_t* arrivals, hipStream_t st) {
+  const int64_t P = T * k;
+  const SendPlan plan = plan_send(P, E);
+  const size_t lds = (size_t(kSendWaves) * E + E + 17 + size_t(plan.nb) * E) * sizeof(int32_t);
+  return launch(send_rank_kernel<false, kSendThreads, kSendItems>, dim3(plan.nb),
+                dim3(kSendThreads), lds, st, topk_idx, P, E, k, nbits_for(E), plan.chunk, plan.nb,
+                mat, arrivals, E / R, R, counts, offsets, rank_offsets, pair_row, row_token);
+}
+
 int enqueue_send(const int32_t* topk_idx, int64_t T, int32_t E, int32_t k, int32_t R,
                  int32_t* counts, int32_t* offsets, int32_t* pair_row, int32_t* row_token,
                  int32_t* rank_offsets, void* workspace, hipStream_t st) {
@@ -1332,23 +1424,21 @@ int enqueue_send(const int32_t* topk_idx, int64_t T, int32_t E, int32_t k, int32
   const size_t lds = (size_t(waves) * E + E + 17 + (plan.fused ? 0 : size_t(plan.nb) * E)) *
                      sizeof(int32_t);
   if (plan.fused) {
-    const int32_t* none = nullptr;
+    int32_t* none = nullptr;
+    uint32_t* no_arrivals = nullptr;
     if (plan.threads == kSendWideThreads)
       return launch(send_rank_kernel<true, kSendWideThreads, kSendItems>, dim3(1),
                     dim3(kSendWideThreads), lds, st, topk_idx, P, E, k, nbits, plan.chunk, 1, none,
-                    L, R, counts, offsets, rank_offsets, pair_row, row_token);
+                    no_arrivals, L, R, counts, offsets, rank_offsets, pair_row, row_token);
     return launch(send_rank_kernel<true, kSendThreads, kSendItems>, dim3(1), dim3(kSendThreads),
-                  lds, st, topk_idx, P, E, k, nbits, plan.chunk, 1, none, L, R, counts, offsets,
-                  rank_offsets, pair_row, row_token);
+                  lds, st, topk_idx, P, E, k, nbits, plan.chunk, 1, none, no_arrivals, L, R,
+                  counts, offsets, rank_offsets, pair_row, row_token);
   }
   int32_t* ws = static_cast<int32_t*>(workspace);
-  const int rc = launch(send_hist_kernel, dim3(plan.nb), dim3(kSendThreads), size_t(E) * 4, st,
-                        topk_idx, P, E, nbits, plan.chunk, ws);
+  const int rc = enqueue_send_hist(topk_idx, T, E, k, ws, st);
   if (rc != MOE_OK) return rc;
-  return launch(send_rank_kernel<false, kSendThreads, kSendItems>, dim3(plan.nb),
-                dim3(kSendThreads), lds, st, topk_idx, P,
-                E, k, nbits, plan.chunk, plan.nb, static_cast<const int32_t*>(ws), L, R, counts,
-                offsets, rank_offsets, pair_row, row_token);
+  return enqueue_send_ranks(topk_idx, T, E, k, R, counts, offsets, pair_row, row_token,
+                            rank_offsets, ws, nullptr, st);
 }
 
 int enqueue_recv(const void* x, const int32_t* pair_row, int64_t T, int32_t H, int32_t k,
@@ -1382,8 +1472,10 @@ int enqueue_recv_fp8(const void* x, const int32_t* pair_row, int64_t T, int32_t 
                 static_cast<uint8_t*>(buf_q), buf_s, capacity);
 }
 
-// Workspace of moe_route_dispatch: the arrival counter of the fused route +
-// send launch, then the send workspace.
+// Workspace of moe_route_dispatch: a block of arrival counters (word 0: the
+// fused route + send launch; word 1: the rank kernel, whose last block
+// zeroes the histogram matrix), then the send workspace.  All of it holds
+// zeros between calls.
 constexpr size_t kArrivalBytes = 256;
 
 bool route_send_fusable(int64_t T, int32_t E, int32_t k) {
@@ -1532,12 +1624,32 @@ int moe_route_dispatch(const float* logits, const void* x, int64_t T, int32_t E,
     st = enqueue_route_send(logits, T, E, k, n_group, topk_group, num_vranks, topk_idx, topk_w,
                             static_cast<uint32_t*>(workspace), expert_counts, expert_offsets,
                             pair_row, row_token, rank_offsets, s);
-  } else {
+    if (st != MOE_OK) return st;
+    return enqueue_recv(x, pair_row, T, H, k, buf, capacity, s);
+  }
+  const SendPlan plan = plan_send(T * k, E);
+  if (plan.fused) {  // single-block send: no histogram matrix
     st = enqueue_route(logits, T, E, k, n_group, topk_group, topk_idx, topk_w, s);
     if (st == MOE_OK)
       st = enqueue_send(topk_idx, T, E, k, num_vranks, expert_counts, expert_offsets, pair_row,
-                        row_token, rank_offsets, ws + kArrivalBytes, s);
+                        row_token, rank_offsets, nullptr, s);
+    if (st != MOE_OK) return st;
+    return enqueue_recv(x, pair_row, T, H, k, buf, capacity, s);
   }
+  // Multi-block send.  The histogram matrix in the workspace holds zeros
+  // between calls.  With enough experts the routing kernel counts the pairs
+  // into it (its atomics then spread over enough addresses); otherwise the
+  // histogram kernel fills it.  The rank kernel reads it, and its last block
+  // zeroes it again.
+  int32_t* mat = reinterpret_cast<int32_t*>(ws + kArrivalBytes);
+  uint32_t* rank_arrivals = static_cast<uint32_t*>(workspace) + 1;
+  const bool count = E >= kRouteCountMinE;
+  st = enqueue_route(logits, T, E, k, n_group, topk_group, topk_idx, topk_w, s,
+                     count ? mat : nullptr, plan.chunk);
+  if (st == MOE_OK && !count) st = enqueue_send_hist(topk_idx, T, E, k, mat, s);
+  if (st == MOE_OK)
+    st = enqueue_send_ranks(topk_idx, T, E, k, num_vranks, expert_counts, expert_offsets, pair_row,
+                            row_token, rank_offsets, mat, rank_arrivals, s);
   if (st != MOE_OK) return st;
   return enqueue_recv(x, pair_row, T, H, k, buf, capacity, s);
 }

@@ -202,15 +202,20 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int64_t T, int32_t E,
  *
  * Small batches (T <= 2048 and T*k <= 4096) route and send in one launch:
  * the last routing block to finish runs the single-block send, found with an
- * arrival counter at the start of the workspace.
+ * arrival counter at the start of the workspace.  Larger batches with
+ * E >= 128 skip the histogram launch: the routing kernel counts every pair
+ * into the send histogram in the workspace, and the last block of the rank
+ * kernel zeroes it again.
  *
  *   workspace  moe_route_dispatch_workspace_bytes(T, E, k) bytes (4-byte
- *              aligned).  Its first 4 bytes must be zero before the first
- *              call that uses it (e.g. hipMemset, torch.zeros); every call
- *              leaves them zero again.  Calls that share a workspace must be
- *              ordered on one stream, and it must not be passed to the other
- *              dispatch calls, whose workspace use would overwrite the
- *              counter.
+ *              aligned).  All of it must be zero before the first call that
+ *              uses it (e.g. hipMemset, torch.zeros); every call that
+ *              returns MOE_OK leaves it zero again once its work has run, so
+ *              it can serve the next call of any size it is large enough
+ *              for.  After MOE_ERR_HIP, zero it again.  Calls that share a
+ *              workspace must be ordered on one stream, and it must not be
+ *              passed to the other dispatch calls, which leave counts in
+ *              theirs.
  * Errors: as the three calls; MOE_ERR_WORKSPACE for a NULL or short
  *         workspace (T > 0).
  */
@@ -225,7 +230,7 @@ int moe_route_dispatch(const float* logits, const void* x, int64_t T, int32_t E,
 
 /*
  * moe_route_dispatch_workspace_bytes - the workspace moe_route_dispatch
- * needs for (T, E, k): a 256-byte arrival counter block followed by the
+ * needs for (T, E, k): a 256-byte block of arrival counters followed by the
  * moe_dispatch_send workspace.  Returns 0 for arguments moe_route_topk would
  * reject.
  */

@@ -125,7 +125,7 @@ static void gpu_checks(void) {
     HIPCHECK(hipMalloc((void**)&d_roff2, sizeof(int32_t) * (R + 1)));
     HIPCHECK(hipMalloc(&d_buf2, 2 * (size_t)P * H));
     HIPCHECK(hipMalloc(&d_ws2, rwsb));
-    HIPCHECK(hipMemset(d_ws2, 0, rwsb)); /* the arrival counter starts at zero */
+    HIPCHECK(hipMemset(d_ws2, 0, rwsb)); /* the workspace starts zeroed */
     for (int rep = 0; rep < 2; ++rep)
       CHECK(moe_route_dispatch(d_logits, d_x, T, E, K, 1, 1, H, R, d_idx2, d_w2, d_counts2, d_off2,
                                d_pr2, d_rt2, d_roff2, d_buf2, P, d_ws2, rwsb, NULL) == MOE_OK);
@@ -133,7 +133,7 @@ static void gpu_checks(void) {
     int32_t* i2 = malloc(sizeof(int32_t) * P);
     int32_t* r2 = malloc(sizeof(int32_t) * P);
     uint16_t* b2 = malloc(2 * (size_t)P * H);
-    uint32_t counter = 1;
+    unsigned char* wsh = malloc(rwsb);
     HIPCHECK(hipMemcpy(i2, d_idx2, sizeof(int32_t) * P, hipMemcpyDeviceToHost));
     CHECK(memcmp(i2, idx, sizeof(int32_t) * P) == 0);
     HIPCHECK(hipMemcpy(i2, d_pr2, sizeof(int32_t) * P, hipMemcpyDeviceToHost));
@@ -142,9 +142,9 @@ static void gpu_checks(void) {
     CHECK(memcmp(r2, rt, sizeof(int32_t) * P) == 0);
     HIPCHECK(hipMemcpy(b2, d_buf2, 2 * (size_t)P * H, hipMemcpyDeviceToHost));
     CHECK(memcmp(b2, buf, 2 * (size_t)P * H) == 0);
-    HIPCHECK(hipMemcpy(&counter, d_ws2, sizeof(counter), hipMemcpyDeviceToHost));
-    CHECK(counter == 0);
-    free(i2); free(r2); free(b2);
+    HIPCHECK(hipMemcpy(wsh, d_ws2, rwsb, hipMemcpyDeviceToHost));
+    for (size_t i = 0; i < rwsb; ++i) CHECK(wsh[i] == 0); /* and every call leaves it so */
+    free(i2); free(r2); free(b2); free(wsh);
     hipFree(d_w2); hipFree(d_idx2); hipFree(d_counts2); hipFree(d_off2); hipFree(d_pr2);
     hipFree(d_rt2); hipFree(d_roff2); hipFree(d_buf2); hipFree(d_ws2);
   }

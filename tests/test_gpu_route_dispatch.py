@@ -1,7 +1,7 @@
 """moe_route_dispatch (route + send + recv in one call; small batches route
 and send in one launch) against the separate calls and the oracle: every
-output bit-identical, the workspace's arrival counter back at zero after
-every call, and graph replays equal to eager calls."""
+output bit-identical, the workspace back at zero after every call, and
+graph replays equal to eager calls."""
 import numpy as np
 import pytest
 import torch
@@ -85,30 +85,74 @@ def test_route_dispatch_shapes(T, E, k, R):
     assert np.array_equal(host(got[0]), r_idx)
 
 
-def test_arrival_counter_returns_to_zero_across_calls():
-    """One workspace reused by calls of varying size (one launch and
-    separate launches) on one stream: each call matches the separate calls
-    and the counter is zero after each."""
+def test_workspace_returns_to_zero_across_calls():
+    """One workspace reused by calls of varying size on one stream: route and
+    send in one launch (arrival counter), and separate launches where the
+    routing kernel counts into the histogram matrix and recv clears it
+    (one wave per token below 2049 tokens, lane groups above).  Repeated
+    sizes would count twice if a clear were missed.  Each call matches the
+    separate calls, and the whole workspace is zero after each."""
     m = _m()
     E, k, R, H = 256, 8, 32, 64
-    wsb = m.moe_route_dispatch_workspace_bytes(4096, E, k)
+    wsb = m.moe_route_dispatch_workspace_bytes(8192, E, k)
     ws = torch.zeros((wsb,), dtype=torch.uint8, device=DEV)
-    for i, T in enumerate([128, 300, 64, 4096, 1, 511, 2000, 200]):
+    for i, T in enumerate([128, 300, 4096, 4096, 64, 600, 600, 8192, 1, 511, 2000, 2000, 3001,
+                           200]):
         lg, xb = _inputs(T, E, H, 100 + i)
         logits, x = dev_f32(lg), dev_bf16(xb)
         got = m.moe_route_dispatch(logits, x, k, R, workspace=ws)
         ref = _separate(m, logits, x, k, E, R)
         torch.cuda.synchronize()
         _same(got, ref)
-        assert int(ws[:4].view(torch.int32).item()) == 0, T
+        assert int(ws.count_nonzero().item()) == 0, T
 
 
-def test_route_dispatch_graph_replays():
+@pytest.mark.parametrize("E,k,R", [(64, 8, 8), (127, 4, 1), (128, 8, 16), (1024, 8, 32)])
+def test_workspace_zero_around_the_counting_threshold(E, k, R):
+    """Multi-block sends on both sides of the expert count from which the
+    routing kernel counts the histogram itself (below it the histogram
+    kernel fills the matrix, and the rank kernel zeroes it either way):
+    repeated calls of two sizes on one workspace."""
+    m = _m()
+    ws = torch.zeros((m.moe_route_dispatch_workspace_bytes(4096, E, k),), dtype=torch.uint8,
+                     device=DEV)
+    for i, T in enumerate([4096, 4096, 1500, 1500, 4096]):
+        print(f"[route_dispatch] workspace E={E} T={T} k={k}", flush=True)
+        lg, xb = _inputs(T, E, 64, 7 * E + i)
+        logits, x = dev_f32(lg), dev_bf16(xb)
+        got = m.moe_route_dispatch(logits, x, k, R, workspace=ws)
+        ref = _separate(m, logits, x, k, E, R)
+        torch.cuda.synchronize()
+        _same(got, ref)
+        assert int(ws.count_nonzero().item()) == 0, (E, T)
+
+
+@pytest.mark.parametrize("T,E,k,R", [(3000, 8, 1, 8), (4096, 8, 1, 1)])
+def test_route_dispatch_single_block_send_above_one_wave_routing(T, E, k, R):
+    """T above 2048 with T*k <= 4096: lane-group routing without counting,
+    then the single-block send."""
+    m = _m()
+    print(f"[route_dispatch] T={T} E={E} k={k} R={R}", flush=True)
+    lg, xb = _inputs(T, E, 64, T + E)
+    logits, x = dev_f32(lg), dev_bf16(xb)
+    ws = torch.zeros((m.moe_route_dispatch_workspace_bytes(T, E, k),), dtype=torch.uint8,
+                     device=DEV)
+    for _ in range(2):
+        got = m.moe_route_dispatch(logits, x, k, R, workspace=ws)
+        ref = _separate(m, logits, x, k, E, R)
+        torch.cuda.synchronize()
+        _same(got, ref)
+        assert int(ws.count_nonzero().item()) == 0
+
+
+@pytest.mark.parametrize("T", [200, 4096])
+def test_route_dispatch_graph_replays(T):
     """The call captured once into a HIP graph and replayed three times, with
     eager work and a synchronisation between replays: every replay equals
-    the eager result."""
+    the eager result and leaves the workspace zero (one launch for route and
+    send at 200 tokens; the counting route and the clearing recv at 4096)."""
     m = _m()
-    T, E, k, R, H = 200, 256, 8, 32, 128
+    E, k, R, H = 256, 8, 32, 128
     lg, xb = _inputs(T, E, H, 5)
     logits, x = dev_f32(lg), dev_bf16(xb)
     bufs = m.MoeBuffers(T, H, E, k, R)
@@ -131,7 +175,7 @@ def test_route_dispatch_graph_replays():
         torch.cuda.synchronize()
         assert torch.equal(bufs.topk_idx[:T], eager[0])
         assert torch.equal(bufs.buf[: T * k].view(torch.int16), eager[1].view(torch.int16))
-        assert int(bufs.route_workspace[:4].view(torch.int32).item()) == 0
+        assert int(bufs.route_workspace.count_nonzero().item()) == 0
 
 
 @pytest.mark.parametrize("T,E,k,G,TG,R", [
