@@ -645,10 +645,13 @@ constexpr int64_t kSendFusedMaxPairs = 4096;
 // per-wave counts take 16 * E ints of LDS, hence the limit on E).
 constexpr int kSendWideThreads = 1024;
 constexpr int kSendWideMaxE = 512;
-constexpr int64_t kSendChunkTarget = 2048;
+// Multi-block send: about kSendChunkTarget pairs per block, kSendRankItems
+// per lane (8 waves), at most kSendMatrixInts counts in the [block][expert]
+// histogram matrix.
+constexpr int64_t kSendChunkTarget = 1024;
+constexpr int kSendRankItems = 2;
 constexpr int kSendMaxBlocks = 64;
-constexpr int kSendMatrixInts = 8192;  // [block][expert] counts staged in LDS by the rank kernel
-constexpr int kLdsInts = 16384;        // 64 KiB of LDS per block at most
+constexpr int kSendMatrixInts = 16384;
 
 struct SendPlan {
   bool fused;
@@ -671,8 +674,6 @@ SendPlan plan_send(int64_t P, int E) {
   }
   int64_t nb = (P + kSendChunkTarget - 1) / kSendChunkTarget;
   int64_t nb_max = kSendMatrixInts / E;
-  const int64_t nb_lds = (kLdsInts - (kSendWaves + 1) * E - 17) / E;  // rank kernel's LDS
-  if (nb_max > nb_lds) nb_max = nb_lds;
   if (nb_max > kSendMaxBlocks) nb_max = kSendMaxBlocks;
   if (nb > nb_max) nb = nb_max;
   if (nb < 1) nb = 1;
@@ -708,15 +709,15 @@ __global__ __launch_bounds__(kSendThreads) void send_hist_kernel(const int32_t* 
   __syncthreads();
   int64_t a, b;
   wave_range(P, chunk, blockIdx.x, a, b);
-  for (int64_t s0 = a; s0 < b; s0 += kWave * kSendItems) {
-    int ev[kSendItems];
+  for (int64_t s0 = a; s0 < b; s0 += kWave * kSendRankItems) {
+    int ev[kSendRankItems];
 #pragma unroll
-    for (int u = 0; u < kSendItems; ++u) {
+    for (int u = 0; u < kSendRankItems; ++u) {
       const int64_t p = s0 + u * kWave + lane_id();
       ev[u] = p < b ? idx[p] : -1;
     }
 #pragma unroll
-    for (int u = 0; u < kSendItems; ++u) {
+    for (int u = 0; u < kSendRankItems; ++u) {
       const int e = ev[u];
       const bool valid = uint32_t(e) < uint32_t(E);
       const uint64_t peers = same_expert_lanes(e, valid, nbits);
@@ -745,16 +746,17 @@ __device__ __forceinline__ void send_rank_block(
     int R, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ rank_offsets, int32_t* __restrict__ pair_row,
     int32_t* __restrict__ row_token) {
-  // LDS: [W][E] per-wave counts | [E] base | [17] scratch | [nb][E] matrix (multi-block)
+  // LDS: [W][E] per-wave counts | [E] base | [17] scratch | [2][THREADS]
+  // partial column sums (multi-block)
   constexpr int nwaves = THREADS / kWave;  // launched with THREADS threads (at most 16 waves)
   const int wid = threadIdx.x / kWave;
   int32_t* hist = sm;
   int32_t* base = sm + nwaves * E;
   int32_t* scratch = base + E;
-  int32_t* mat = scratch + 17;
+  int32_t* part = scratch + 17;
   int64_t a, b;
   wave_range(P, chunk, bid, a, b);
-  // The first step's expert indices are requested before the matrix staging
+  // The first step's expert indices are requested before the matrix loads
   // below, so the two memory round trips overlap.
   int ev0[ITEMS];
 #pragma unroll
@@ -763,51 +765,62 @@ __device__ __forceinline__ void send_rank_block(
     ev0[u] = p < b ? idx[p] : -1;
   }
   for (int i = threadIdx.x; i < nwaves * E; i += blockDim.x) hist[i] = 0;
+  // Multi-block: each expert's total and this block's prefix (the blocks
+  // before it), summed straight from the [block][expert] histogram matrix
+  // (L2-resident) with one batch of independent loads per thread.  Up to
+  // THREADS experts, G threads share a column, each summing every G-th row,
+  // and their partial sums meet in LDS; above that (E <= 2 * THREADS) each
+  // thread sums two columns.
+  int32_t pre[2] = {0, 0};
+  const bool shared_cols = E <= THREADS;
   if (!FUSED) {
-    // The [block][expert] histogram matrix (a few KiB, L2-resident), staged
-    // with batches of independent coalesced loads.
-    constexpr int kBatch = 16;
-    const int n = nb * E;
-    for (int i0 = threadIdx.x; i0 < n; i0 += THREADS * kBatch) {
-      int32_t v[kBatch];
+    constexpr int kBatch = 32;
+    const int G = shared_cols ? min(THREADS / E, nb) : 1;
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int i = i0 + u * THREADS;
-        v[u] = i < n ? ws_cnt[i] : 0;
+    for (int q = 0; q < 2; ++q) {
+      const int e = shared_cols ? int(threadIdx.x) % E : int(threadIdx.x) + q * THREADS;
+      const int g = shared_cols ? int(threadIdx.x) / E : 0;
+      if ((shared_cols && q > 0) || e >= E || g >= G) continue;
+      int32_t tot = 0, before = 0;
+      for (int r0 = g; r0 < nb; r0 += G * kBatch) {
+        int32_t v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int r = r0 + u * G;
+          v[u] = r < nb ? ws_cnt[r * E + e] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          tot += v[u];
+          before += r0 + u * G < bid ? v[u] : 0;
+        }
       }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int i = i0 + u * THREADS;
-        if (i < n) mat[i] = v[u];
+      if (shared_cols) {
+        part[threadIdx.x] = tot;
+        part[THREADS + threadIdx.x] = before;
+      } else {
+        base[e] = tot;
+        pre[q] = before;
       }
     }
   }
   __syncthreads();
-  // Every thread's matrix loads have returned (their values are in LDS), so
+  // Every thread's matrix loads have returned (their sums are in LDS), so
   // the block may count in; the result is first needed after pass 1.
   __shared__ int32_t clear_mat;
   uint32_t arrived_before = 0u;
   if (!FUSED && arrivals != nullptr && threadIdx.x == 0)
     arrived_before =
         __hip_atomic_fetch_add(arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
-  // Multi-block: totals per expert and this block's prefix.  E <= 2 * blockDim.
-  int32_t pre[2] = {0, 0};
-  if (!FUSED) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int e = threadIdx.x + q * THREADS;
-      if (e < E) {
-        int32_t tot = 0, before = 0;
-        for (int r = 0; r < nb; ++r) {
-          const int32_t c = mat[r * E + e];
-          tot += c;
-          before += r < bid ? c : 0;
-        }
-        base[e] = tot;
-        pre[q] = before;
-      }
+  if (!FUSED && shared_cols && int(threadIdx.x) < E) {
+    const int G = min(THREADS / E, nb);
+    int32_t tot = 0, before = 0;
+    for (int g = 0; g < G; ++g) {
+      tot += part[g * E + threadIdx.x];
+      before += part[THREADS + g * E + threadIdx.x];
     }
+    base[threadIdx.x] = tot;
+    pre[0] = before;
   }
 
   int32_t* my_hist = hist + wid * E;
@@ -1407,8 +1420,8 @@ int enqueue_send_ranks(const int32_t* topk_idx, int64_t T, int32_t E, int32_t k,
                        int32_t* rank_offsets, int32_t* mat, uint32_t* arrivals, hipStream_t st) {
   const int64_t P = T * k;
   const SendPlan plan = plan_send(P, E);
-  const size_t lds = (size_t(kSendWaves) * E + E + 17 + size_t(plan.nb) * E) * sizeof(int32_t);
-  return launch(send_rank_kernel<false, kSendThreads, kSendItems>, dim3(plan.nb),
+  const size_t lds = (size_t(kSendWaves) * E + E + 17 + 2 * kSendThreads) * sizeof(int32_t);
+  return launch(send_rank_kernel<false, kSendThreads, kSendRankItems>, dim3(plan.nb),
                 dim3(kSendThreads), lds, st, topk_idx, P, E, k, nbits_for(E), plan.chunk, plan.nb,
                 mat, arrivals, E / R, R, counts, offsets, rank_offsets, pair_row, row_token);
 }
@@ -1420,10 +1433,8 @@ int enqueue_send(const int32_t* topk_idx, int64_t T, int32_t E, int32_t k, int32
   const SendPlan plan = plan_send(P, E);
   const int nbits = nbits_for(E);
   const int L = E / R;
-  const int waves = plan.fused ? plan.threads / kWave : kSendWaves;
-  const size_t lds = (size_t(waves) * E + E + 17 + (plan.fused ? 0 : size_t(plan.nb) * E)) *
-                     sizeof(int32_t);
   if (plan.fused) {
+    const size_t lds = (size_t(plan.threads / kWave) * E + E + 17) * sizeof(int32_t);
     int32_t* none = nullptr;
     uint32_t* no_arrivals = nullptr;
     if (plan.threads == kSendWideThreads)
