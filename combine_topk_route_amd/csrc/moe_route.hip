@@ -229,6 +229,11 @@ __device__ __forceinline__ float key_value(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
+// s_waitcnt operand that waits for every vector memory operation of the wave
+// (vmcnt 0) and leaves the export and LDS/scalar counters unconstrained:
+// vmcnt bits [3:0] and [15:14] = 0, expcnt [6:4] = 7, lgkmcnt [11:8] = 15.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 constexpr int kRouteWavesPerBlock = 4;
 constexpr int kRouteThreads = kRouteWavesPerBlock * kWave;
 constexpr int64_t kRouteWaveMaxTokens = 2048;  // up to here plain routing uses one wave per token
@@ -958,12 +963,14 @@ __global__ __launch_bounds__(THREADS) void route_send_kernel(
   if (t < T)
     route_wave_token<IPL, GROUPED, false>(logits, t, E, k, n_group, topk_group, topk_idx, topk_w,
                                           nullptr, 1u);
-  // Release the block's routing at device scope before it counts in: each
-  // wave for its own stores, then thread 0 for all that the barrier ordered
-  // before it.  The last block to arrive acquires, so it sees every block's
-  // routing.  (Release and acquire only: a full fence would write the L2
-  // back a second time.)
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  // Release the block's routing at device scope before it counts in.  Each
+  // wave waits until its own stores have reached the L2 (vmcnt 0); after the
+  // barrier, thread 0's agent-scope release writes the L2 back, which then
+  // covers every wave's stores.  The last block to arrive acquires, so it
+  // sees every block's routing.  (One write-back per block: a release in
+  // every wave cost 1.5 us at DSv3 decode, and a full fence would write the
+  // L2 back once more.)
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   if (threadIdx.x == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
