@@ -723,6 +723,7 @@ __global__ __launch_bounds__(kSendThreads) void send_hist_kernel(const int32_t* 
     }
 #pragma unroll
     for (int u = 0; u < kSendRankItems; ++u) {
+      if (s0 + u * kWave >= b) continue;  // wave-uniform: past the wave's range
       const int e = ev[u];
       const bool valid = uint32_t(e) < uint32_t(E);
       const uint64_t peers = same_expert_lanes(e, valid, nbits);
@@ -844,6 +845,9 @@ __device__ __forceinline__ void send_rank_block(
 #pragma unroll
     for (int u = 0; u < ITEMS; ++u) {
       const int64_t p = s0 + u * kWave + lane_id();
+      keep_e[u] = -1;
+      keep_slot[u] = -1;
+      if (s0 + u * kWave >= b) continue;  // wave-uniform: past the wave's range
       const int e = ev[u];
       const bool valid = uint32_t(e) < uint32_t(E);
       const uint64_t peers = same_expert_lanes(e, valid, nbits);
