@@ -137,33 +137,26 @@ def main() -> int:
     x = torch.from_numpy(wl.x.view(np.int16)).view(torch.bfloat16).to(dev)
     y = torch.from_numpy(wl.y.view(np.int16)).view(torch.bfloat16).to(dev)
     del wl
-    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
-    w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    counts = torch.empty((E,), dtype=torch.int32, device=dev)
-    offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
-    pair_row = torch.empty((T, k), dtype=torch.int32, device=dev)
-    row_token = torch.empty((P,), dtype=torch.int32, device=dev)
-    rank_off = torch.empty((R + 1,), dtype=torch.int32, device=dev)
-    ws = torch.empty((max(1, m.moe_dispatch_workspace_bytes(T, E, k)),), dtype=torch.uint8,
-                     device=dev)
-    rws = torch.zeros((m.moe_route_dispatch_workspace_bytes(T, E, k),), dtype=torch.uint8,
-                      device=dev)
-    buf = torch.empty((P, H), dtype=torch.bfloat16, device=dev)
-    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    # One set of preallocated buffers (the allocation-free API a serving loop
+    # uses); the per-entry-point breakdown below writes into the same tensors.
+    bufs = m.MoeBuffers(T, H, E, k, R, device=dev)
+    idx, w = bufs.topk_idx, bufs.topk_w
+    counts, offsets, rank_off = bufs.expert_counts, bufs.expert_offsets, bufs.rank_offsets
+    pair_row, row_token = bufs.pair_row, bufs.row_token
+    ws = bufs.workspace
+    buf, out = bufs.buf, bufs.out
     stream = torch.cuda.current_stream()
 
     def step(ev=None, st=None):
         """route -> send -> recv -> combine.  Without events, route, send and
         recv go through the one moe_route_dispatch call (the same kernels,
         route and send in one launch for small batches) and combine through
-        moe_combine; with events, each entry point is bracketed on its own."""
+        moe_combine, both by way of MoeBuffers; with events, each entry point
+        is bracketed on its own."""
         st = stream if st is None else st
         if ev is None:
-            m.moe_route_dispatch(logits, x, k, R, topk_idx=idx, topk_w=w, buf=buf,
-                                 expert_counts=counts, expert_offsets=offsets, pair_row=pair_row,
-                                 row_token=row_token, rank_offsets=rank_off, workspace=rws,
-                                 stream=st)
-            m.moe_combine(y, pair_row, w, out=out, stream=st)
+            _, tw, send, _ = bufs.route_dispatch(logits, x, stream=st)
+            bufs.combine(y, send.pair_row, tw, stream=st)
             return
         ev[0].record(st)
         m.moe_route_topk(logits, k, topk_idx=idx, topk_w=w, stream=st)

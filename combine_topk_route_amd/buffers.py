@@ -14,6 +14,7 @@ from typing import Optional
 
 import torch
 
+from . import _lib
 from . import binding as _b
 
 
@@ -31,6 +32,7 @@ class MoeBuffers:
                  fp8: bool = False):
         dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
         self.max_tokens, self.H, self.E, self.k, self.R = max_tokens, hidden, num_experts, k, num_vranks
+        self.device_index = dev.index if dev.index is not None else torch.cuda.current_device()
         cap = max_tokens * k
         i32, f32 = torch.int32, torch.float32
         self.topk_idx = torch.empty((max_tokens, k), dtype=i32, device=dev)
@@ -92,16 +94,20 @@ class MoeBuffers:
     def route_dispatch(self, logits: torch.Tensor, x: torch.Tensor, n_group: int = 1,
                        topk_group: int = 1, stream=None):
         """Route + send + receive in one call; returns (topk_idx, topk_w,
-        SendResult, buf [T*k, H])."""
-        v = self._v(x.shape[0])
-        s = v.send
-        _b.moe_route_dispatch(logits, x, self.k, self.R, n_group=n_group, topk_group=topk_group,
-                              topk_idx=v.topk_idx, topk_w=v.topk_w, buf=v.buf,
-                              expert_counts=s.expert_counts, expert_offsets=s.expert_offsets,
-                              pair_row=s.pair_row, row_token=s.row_token,
-                              rank_offsets=s.rank_offsets, workspace=self.route_workspace,
-                              stream=stream)
-        return v.topk_idx, v.topk_w, s, v.buf
+        SendResult, buf [T*k, H]).  Only ``logits`` and ``x`` are checked per
+        call: the outputs are this object's own buffers, whose pointers the
+        views keep."""
+        T = x.shape[0]
+        v = self._v(T)
+        d = self.device_index
+        lp = _b._dev(logits, "logits", torch.float32, 2, device=d)
+        xp = _b._dev(x, "x", torch.bfloat16, 2, device=d)
+        if logits.shape[0] != T or logits.shape[1] != self.E or x.shape[1] != self.H:
+            raise ValueError(f"logits must be [T, {self.E}] and x [T, {self.H}]")
+        _b._check("moe_route_dispatch", _lib.load().moe_route_dispatch(
+            lp, xp, T, self.E, self.k, n_group, topk_group, self.H, self.R, *v.route_dispatch_args,
+            _b._stream(stream, x)))
+        return v.topk_idx, v.topk_w, v.send, v.buf
 
     def dispatch_fp8(self, topk_idx: torch.Tensor, x: torch.Tensor, stream=None):
         """Send + fp8 receive; returns (SendResult, codes [T*k, H], scales [T*k, H/128])."""
@@ -120,11 +126,21 @@ class MoeBuffers:
     def combine(self, y: torch.Tensor, pair_row: torch.Tensor, topk_w: torch.Tensor,
                 stream=None) -> torch.Tensor:
         v = self._v(pair_row.shape[0])
-        return _b.moe_combine(y, pair_row, topk_w, out=v.out, stream=stream)
+        if pair_row is not v.send.pair_row or topk_w is not v.topk_w:
+            return _b.moe_combine(y, pair_row, topk_w, out=v.out, stream=stream)
+        # This object's own routing views: only y is checked per call.
+        yp = _b._dev(y, "y", torch.bfloat16, 2, device=self.device_index)
+        if y.shape[1] != self.H:
+            raise ValueError(f"y must be [capacity, {self.H}]")
+        _b._check("moe_combine", _lib.load().moe_combine(
+            yp, v.pair_row_ptr, v.topk_w_ptr, v.T, self.H, self.k, y.shape[0], v.out_ptr,
+            _b._stream(stream, y)))
+        return v.out
 
 
 class _Views:
-    """MoeBuffers' tensors cut to a batch of T tokens."""
+    """MoeBuffers' tensors cut to a batch of T tokens, and their device
+    pointers in the order the C entry points take them."""
 
     def __init__(self, b: MoeBuffers, T: int):
         self.T = T
@@ -133,3 +149,12 @@ class _Views:
         self.out = b.out[:T]
         self.send = _b.SendResult(b.expert_counts, b.expert_offsets, b.pair_row[:T],
                                   b.row_token[: T * b.k], b.rank_offsets)
+        s = self.send
+        self.route_dispatch_args = (
+            self.topk_idx.data_ptr(), self.topk_w.data_ptr(), s.expert_counts.data_ptr(),
+            s.expert_offsets.data_ptr(), s.pair_row.data_ptr(), s.row_token.data_ptr(),
+            s.rank_offsets.data_ptr(), self.buf.data_ptr(), T * b.k,
+            b.route_workspace.data_ptr(), b.route_workspace.numel())
+        self.pair_row_ptr = s.pair_row.data_ptr()
+        self.topk_w_ptr = self.topk_w.data_ptr()
+        self.out_ptr = self.out.data_ptr()
