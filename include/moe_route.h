@@ -114,9 +114,9 @@ int moe_route_topk_grouped(const float* logits, int64_t T, int32_t E, int32_t k,
 
 /*
  * moe_dispatch_workspace_bytes - device scratch moe_dispatch_send needs for
- * (T, E, k): per-block per-expert counts for the multi-block scan.  0 means
- * no workspace is needed (workspace may then be NULL).  Returns 0 as well for
- * arguments moe_dispatch_send would reject.
+ * (T, E, k): per-block per-expert counts for the multi-block scan, at most
+ * 64 KiB.  0 means no workspace is needed (T*k <= 4096; workspace may then
+ * be NULL).  Returns 0 as well for arguments moe_dispatch_send would reject.
  */
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k);
 
