@@ -33,10 +33,14 @@
 //                        which every block scans for itself.  Small inputs run
 //                        histogram, scan and slots in one block of 8 or 16
 //                        waves.
-//   route_send_kernel    small batches: routing (one wave per token) and the
-//                        single-block send in one launch; the last block to
-//                        finish routing, found with a device-scope arrival
-//                        counter, runs the send.
+//   send_recv_kernel     small batches (T*k <= 2048, k <= 8): block 0 runs the
+//                        single-block send while the other blocks copy rows,
+//                        each finding its token's k rows from topk_idx with
+//                        ballot counts (lower experts, earlier equal ones).
+//   route_send_kernel    small batches up to T*k = 4096: routing (one wave per
+//                        token) and the single-block send in one launch; the
+//                        last block to finish routing, found with a
+//                        device-scope arrival counter, runs the send.
 //   dispatch_recv_kernel one block per (token, 1 KiB column slice); each wave
 //                        copies the slice to one of the token's k rows: a
 //                        cached 16-byte load (the block's waves share it) and
@@ -1042,6 +1046,99 @@ __global__ __launch_bounds__(kMaxRowThreads) void dispatch_recv_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// send and recv in one launch for small batches
+// ---------------------------------------------------------------------------
+
+constexpr int64_t kSendRecvMaxPairs = int64_t(kSendWaves) * kWave * kSendItems;  // one 8-wave step
+constexpr int kSendRecvMaxK = kSendWaves;  // one wave per destination row
+constexpr int kSendRecvSlices = 8;         // 1 KiB slices of a row per copy unit
+
+// Block 0 runs the single-block send.  Every other block copies up to 8
+// slices of one token's row to the token's k rows, and finds each row
+// itself: the row of pair (t, j) with expert e is the number of pairs with a
+// lower expert (e's offset) plus the number of earlier pairs with expert e
+// (its slot in the stable order).  The block counts both over topk_idx with
+// ballots, so the counts are wave-uniform and need no reduction inside a
+// wave.  The copies never wait for the send, which runs beside them.
+// Wave w copies to destination w (k <= 8).
+__global__ __launch_bounds__(kSendThreads) void send_recv_kernel(
+    const int32_t* __restrict__ idx, int64_t T, int E, int k, int nbits, int L, int R,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ pair_row,
+    int32_t* __restrict__ row_token, const u32x4* __restrict__ x, int C, int nparts,
+    int64_t units, u32x4* __restrict__ buf, int64_t capacity) {
+  extern __shared__ int32_t sm[];
+  const int64_t P = T * k;
+  if (blockIdx.x == 0) {
+    send_rank_block<true, kSendThreads, kSendItems>(0, sm, idx, P, E, k, nbits, P, 1, nullptr,
+                                                    nullptr, L, R, counts, offsets, rank_offsets,
+                                                    pair_row, row_token);
+    return;
+  }
+  __shared__ uint32_t part[kSendWaves][2 * kSendRecvMaxK];  // per-wave counts
+  __shared__ int32_t rows[kSendRecvMaxK];
+  const int lane = lane_id();
+  const int wid = threadIdx.x / kWave;
+  for (int64_t unit = blockIdx.x - 1; unit < units; unit += gridDim.x - 1) {
+    const int64_t t = unit / nparts;
+    const int sp = int(unit - t * nparts);
+    const int64_t pt = t * k;  // flat index of the token's first pair
+    int ej[kSendRecvMaxK];
+#pragma unroll
+    for (int j = 0; j < kSendRecvMaxK; ++j) ej[j] = j < k ? idx[pt + j] : -1;
+    uint32_t lt[kSendRecvMaxK], eq[kSendRecvMaxK];
+#pragma unroll
+    for (int j = 0; j < kSendRecvMaxK; ++j) lt[j] = eq[j] = 0u;
+    for (int64_t p0 = int64_t(wid) * kWave; p0 < P; p0 += kSendThreads) {  // wave-uniform bounds
+      const int64_t p = p0 + lane;
+      const bool in = p < P;
+      const int v = in ? idx[p] : -1;
+#pragma unroll
+      for (int j = 0; j < kSendRecvMaxK; ++j) {
+        if (j < k) {
+          lt[j] += __popcll(ballot(in && uint32_t(v) < uint32_t(ej[j])));
+          eq[j] += __popcll(ballot(in && v == ej[j] && p < pt + j));
+        }
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < kSendRecvMaxK; ++j) {
+        part[wid][j] = lt[j];
+        part[wid][kSendRecvMaxK + j] = eq[j];
+      }
+    }
+    __syncthreads();
+    if (int(threadIdx.x) < k) {
+      const int j = threadIdx.x;
+      const int e = idx[pt + j];
+      uint32_t r = 0u;
+#pragma unroll
+      for (int w = 0; w < kSendWaves; ++w) r += part[w][j] + part[w][kSendRecvMaxK + j];
+      rows[j] = uint32_t(e) < uint32_t(E) ? int32_t(r) : -1;  // an invalid expert: dropped
+    }
+    __syncthreads();
+    if (wid < k) {
+      const int32_t r = rows[wid];
+      if (uint64_t(int64_t(r)) < uint64_t(capacity)) {
+        u32x4 v[kSendRecvSlices];
+#pragma unroll
+        for (int s = 0; s < kSendRecvSlices; ++s) {
+          const int c = (sp * kSendRecvSlices + s) * kSlice + lane;
+          if (c < C) v[s] = x[t * C + c];
+        }
+#pragma unroll
+        for (int s = 0; s < kSendRecvSlices; ++s) {
+          const int c = (sp * kSendRecvSlices + s) * kSlice + lane;
+          if (c < C) __builtin_nontemporal_store(v[s], &buf[int64_t(r) * C + c]);
+        }
+      }
+    }
+    __syncthreads();  // part and rows are reused by the next unit
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp8 dispatch recv: block-scaled OCP E4M3 payloads
 // ---------------------------------------------------------------------------
 
@@ -1472,6 +1569,28 @@ int enqueue_recv(const void* x, const int32_t* pair_row, int64_t T, int32_t H, i
                 static_cast<u32x4*>(buf), capacity);
 }
 
+// Send + recv in one launch: T*k <= 2048 (the 8-wave single-block send in one
+// step) and k <= 8.
+bool send_recv_fusable(int64_t T, int32_t k) {
+  return T * k <= kSendRecvMaxPairs && k <= kSendRecvMaxK;
+}
+
+int enqueue_send_recv(const int32_t* topk_idx, const void* x, int64_t T, int32_t E, int32_t k,
+                      int32_t H, int32_t R, int32_t* counts, int32_t* offsets, int32_t* pair_row,
+                      int32_t* row_token, int32_t* rank_offsets, void* buf, int64_t capacity,
+                      hipStream_t st) {
+  const int C = H / 8;
+  const int ncs = (C + kSlice - 1) / kSlice;
+  const int nparts = (ncs + kSendRecvSlices - 1) / kSendRecvSlices;
+  const int64_t units = T * nparts;
+  const int64_t copy_blocks = units < kMaxRowBlocks ? units : kMaxRowBlocks;
+  const size_t lds = (size_t(kSendWaves) * E + E + 17) * sizeof(int32_t);
+  return launch(send_recv_kernel, dim3(unsigned(1 + copy_blocks)), dim3(kSendThreads), lds, st,
+                topk_idx, T, E, k, nbits_for(E), E / R, R, counts, offsets, rank_offsets, pair_row,
+                row_token, static_cast<const u32x4*>(x), C, nparts, units,
+                static_cast<u32x4*>(buf), capacity);
+}
+
 int check_fp8_rows(int64_t T, int32_t H, int32_t k, int64_t capacity, const void* x,
                    const void* buf_q, const void* buf_s) {
   const int st = check_rows(T, H, k, capacity, x, buf_q);
@@ -1608,6 +1727,9 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int64_t T, int32_t E, i
   st = check_rows(T, H, k, capacity, x, buf);
   if (st != MOE_OK || T == 0) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (send_recv_fusable(T, k))
+    return enqueue_send_recv(topk_idx, x, T, E, k, H, num_vranks, expert_counts, expert_offsets,
+                             pair_row, row_token, rank_offsets, buf, capacity, s);
   st = enqueue_send(topk_idx, T, E, k, num_vranks, expert_counts, expert_offsets, pair_row,
                     row_token, rank_offsets, workspace, s);
   if (st != MOE_OK) return st;
@@ -1642,6 +1764,12 @@ int moe_route_dispatch(const float* logits, const void* x, int64_t T, int32_t E,
   if (workspace == nullptr || workspace_bytes < kArrivalBytes) return MOE_ERR_WORKSPACE;
   if (!aligned(workspace, 4)) return MOE_ERR_ALIGNMENT;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (send_recv_fusable(T, k)) {  // route, then send and recv in one launch
+    st = enqueue_route(logits, T, E, k, n_group, topk_group, topk_idx, topk_w, s);
+    if (st != MOE_OK) return st;
+    return enqueue_send_recv(topk_idx, x, T, E, k, H, num_vranks, expert_counts, expert_offsets,
+                             pair_row, row_token, rank_offsets, buf, capacity, s);
+  }
   if (route_send_fusable(T, E, k)) {
     st = enqueue_route_send(logits, T, E, k, n_group, topk_group, num_vranks, topk_idx, topk_w,
                             static_cast<uint32_t*>(workspace), expert_counts, expert_offsets,

@@ -179,7 +179,10 @@ int moe_dispatch_recv(const void* x, const int32_t* pair_row, int64_t T,
 /*
  * moe_dispatch - moe_dispatch_send followed by moe_dispatch_recv on one
  * stream; arguments are the union of theirs, with the same meaning.  All
- * arguments of both halves are checked before anything is enqueued.
+ * arguments of both halves are checked before anything is enqueued.  With
+ * T*k <= 2048 and k <= 8 both halves run in one launch (the copies find
+ * their rows from topk_idx themselves; the results are identical), and the
+ * workspace is not used.
  */
 int moe_dispatch(const int32_t* topk_idx, const void* x, int64_t T, int32_t E,
                  int32_t k, int32_t H, int32_t num_vranks,
@@ -200,12 +203,13 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int64_t T, int32_t E,
  * 1 is plain moe_route_topk).  All arguments are checked before anything is
  * enqueued.  The outputs are identical to the separate calls.
  *
- * Small batches (T <= 2048 and T*k <= 4096) route and send in one launch:
- * the last routing block to finish runs the single-block send, found with an
- * arrival counter at the start of the workspace.  Larger batches with
- * E >= 128 skip the histogram launch: the routing kernel counts every pair
- * into the send histogram in the workspace, and the last block of the rank
- * kernel zeroes it again.
+ * Launches, by size: with T*k <= 2048 and k <= 8, routing and then one
+ * launch for send and recv (as moe_dispatch).  Otherwise, with T <= 2048 and
+ * T*k <= 4096, route and send share one launch: the last routing block to
+ * finish runs the single-block send, found with an arrival counter at the
+ * start of the workspace.  Larger batches with E >= 128 skip the histogram
+ * launch: the routing kernel counts every pair into the send histogram in
+ * the workspace, and the last block of the rank kernel zeroes it again.
  *
  *   workspace  moe_route_dispatch_workspace_bytes(T, E, k) bytes (4-byte
  *              aligned).  All of it must be zero before the first call that

@@ -186,6 +186,47 @@ def test_send_drops_out_of_range_experts():
     assert host(res.row_token)[:4].tolist() == [0, 1, 2, 2]
 
 
+@pytest.mark.parametrize("T,k,E,R,H", [
+    (1, 1, 1, 1, 8), (3, 2, 4, 1, 64), (16, 2, 8, 1, 256), (128, 8, 256, 32, 7168),
+    (256, 8, 256, 32, 1032), (300, 6, 40, 8, 8200), (2048, 1, 7, 7, 64), (683, 3, 1000, 8, 136),
+])
+def test_dispatch_in_one_launch_matches_send_then_recv(T, k, E, R, H):
+    """moe_dispatch runs send and recv in one launch for T*k <= 2048 and
+    k <= 8 (block 0 sends; the other blocks find their rows from topk_idx).
+    Against moe_dispatch_send then moe_dispatch_recv, with out-of-range
+    experts (dropped), repeated experts inside a token, spare capacity and
+    canary rows: every output and every buffer byte identical."""
+    m = _m()
+    print(f"[edges] dispatch one launch T={T} k={k} E={E} R={R} H={H}", flush=True)
+    rng = np.random.default_rng(T * 7 + k * 3 + E)
+    idx = rng.integers(0, E, (T, k)).astype(np.int32)
+    drop = rng.random((T, k)) < 0.05
+    idx[drop] = rng.choice(np.array([-1, E, E + 5, -(2 ** 31)], np.int32), int(drop.sum()))
+    if T > 2:
+        idx[1, :] = idx[0, 0] if idx[0, 0] >= 0 else 0   # one expert repeated inside a token
+    x = _rand_bf16((T, H), T + H)
+    cap = T * k + 5
+    canary = np.uint16(0x7FA5)
+    bufs = []
+    for one_call in (True, False):
+        buf = dev_bf16(np.full((cap, H), canary, np.uint16))
+        if one_call:
+            res, _ = m.moe_dispatch(dev_i32(idx), dev_bf16(x), E, R, buf=buf, capacity=cap)
+        else:
+            res = m.moe_dispatch_send(dev_i32(idx), E, R)
+            m.moe_dispatch_recv(dev_bf16(x), res.pair_row, buf=buf, capacity=cap)
+        torch.cuda.synchronize()
+        bufs.append((res, host_bf16(buf)))
+    (a, ba), (b, bb) = bufs
+    n_valid = int(host(a.expert_offsets)[E])   # row_token past this is left untouched
+    for name in ("expert_counts", "expert_offsets", "pair_row", "rank_offsets"):
+        assert np.array_equal(host(getattr(a, name)), host(getattr(b, name))), name
+    assert np.array_equal(host(a.row_token)[:n_valid], host(b.row_token)[:n_valid])
+    assert n_valid == int((idx >= 0).sum() - ((idx >= E).sum()))
+    assert np.array_equal(ba, bb)
+    assert (ba[n_valid:] == canary).all()
+
+
 # ------------------------------------------------------------------ recv / combine
 
 @pytest.mark.parametrize("T,H,k", [(1, 8, 1), (3, 8, 2), (37, 296, 3), (1000, 4096, 2),
