@@ -145,12 +145,13 @@ def test_route_dispatch_single_block_send_above_one_wave_routing(T, E, k, R):
         assert int(ws.count_nonzero().item()) == 0
 
 
-@pytest.mark.parametrize("T", [200, 4096])
+@pytest.mark.parametrize("T", [200, 300, 4096])
 def test_route_dispatch_graph_replays(T):
     """The call captured once into a HIP graph and replayed three times, with
     eager work and a synchronisation between replays: every replay equals
-    the eager result and leaves the workspace zero (one launch for route and
-    send at 200 tokens; the counting route and the clearing recv at 4096)."""
+    the eager result and leaves the workspace zero (200 tokens: routing, then
+    send + recv in one launch; 300: route and send in one launch; 4096: the
+    counting route and the rank kernel that clears the matrix)."""
     m = _m()
     E, k, R, H = 256, 8, 32, 128
     lg, xb = _inputs(T, E, H, 5)
