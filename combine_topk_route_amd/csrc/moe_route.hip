@@ -747,8 +747,9 @@ __global__ __launch_bounds__(kSendThreads) void send_hist_kernel(const int32_t* 
 // over waves and the block base, and writes row_token.
 // The rank step of block `bid` (0 for FUSED), run by a block of THREADS
 // threads; sm: its dynamic LDS.  arrivals (multi-block only; nullptr: keep
-// the matrix): each block counts in once it has staged the histogram matrix,
-// and the last one clears the matrix and the counter for the next call.
+// the matrix): each block counts in once its column sums of the histogram
+// matrix are in LDS, and the last one clears the matrix and the counter for
+// the next call.
 template <bool FUSED, int THREADS, int ITEMS>
 __device__ __forceinline__ void send_rank_block(
     int bid, int32_t* sm, const int32_t* __restrict__ idx, int64_t P, int E, int k, int nbits,
