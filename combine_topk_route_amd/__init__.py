@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     moe_dispatch_send,
     moe_dispatch_workspace_bytes,
     moe_route_dispatch,
+    moe_route_dispatch_fp8,
     moe_route_dispatch_workspace_bytes,
     moe_route_topk,
     moe_route_topk_grouped,

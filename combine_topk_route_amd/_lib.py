@@ -36,6 +36,9 @@ SIGNATURES = {
                                     _c_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp,
                                     _c_size, _vp]),
     "moe_route_dispatch_workspace_bytes": (_c_size, [_c_i64, _c_i32, _c_i32]),
+    "moe_route_dispatch_fp8": (_c_int, [_vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                        _c_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _c_i64, _vp, _c_size, _vp]),
 }
 
 MOE_OK = 0

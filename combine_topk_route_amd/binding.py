@@ -351,6 +351,46 @@ def moe_dispatch_fp8(topk_idx: torch.Tensor, x: torch.Tensor, E: int, num_vranks
     return out, buf_q, buf_scale
 
 
+def moe_route_dispatch_fp8(logits: torch.Tensor, x: torch.Tensor, k: int, num_vranks: int = 1, *,
+                           n_group: int = 1, topk_group: int = 1, topk_idx=None, topk_w=None,
+                           buf_q=None, buf_scale=None, capacity=None, expert_counts=None,
+                           expert_offsets=None, pair_row=None, row_token=None,
+                           rank_offsets=None, with_rank_offsets: bool = True, workspace=None,
+                           stream=None):
+    """Route, send and block-scaled fp8 receive in one call; returns
+    (topk_idx, topk_w, SendResult, buf_q, buf_scale).  The workspace rules
+    are moe_route_dispatch's."""
+    lp = _dev(logits, "logits", torch.float32, 2)
+    d = logits.get_device()
+    xp = _dev(x, "x", torch.bfloat16, 2, device=d)
+    T, E = logits.shape
+    H = x.shape[1]
+    if x.shape[0] != T:
+        raise ValueError("x and logits disagree on T")
+    if topk_idx is None:
+        topk_idx = _empty((T, k), torch.int32, logits)
+    if topk_w is None:
+        topk_w = _empty((T, k), torch.float32, logits)
+    if topk_idx.shape != (T, k) or topk_w.shape != (T, k):
+        raise ValueError("topk_idx / topk_w must be [T, k]")
+    ip = _dev(topk_idx, "topk_idx", torch.int32, device=d)
+    wp = _dev(topk_w, "topk_w", torch.float32, device=d)
+    out = _send_outputs(topk_idx, E, num_vranks, expert_counts, expert_offsets, pair_row,
+                        row_token, rank_offsets, with_rank_offsets)
+    buf_q, buf_scale, capacity = _fp8_bufs(x, T, k, buf_q, buf_scale, capacity)
+    if workspace is None:
+        workspace = torch.zeros((max(1, moe_route_dispatch_workspace_bytes(T, E, k)),),
+                                dtype=torch.uint8, device=logits.device)
+    wsp = _dev(workspace, "workspace", torch.uint8, device=d)
+    cp, op, pp, tp, rp = _send_ptrs(out, d)
+    _check("moe_route_dispatch_fp8", _lib.load().moe_route_dispatch_fp8(
+        lp, xp, T, E, k, n_group, topk_group, H, num_vranks, ip, wp, cp, op, pp, tp, rp,
+        _dev(buf_q, "buf_q", torch.uint8, device=d),
+        _dev(buf_scale, "buf_scale", torch.float32, device=d), capacity, wsp, workspace.numel(),
+        _stream(stream, logits)))
+    return topk_idx, topk_w, out, buf_q, buf_scale
+
+
 def moe_combine(y: torch.Tensor, pair_row: torch.Tensor, topk_w: torch.Tensor,
                 out: Optional[torch.Tensor] = None, capacity: Optional[int] = None,
                 stream=None) -> torch.Tensor:

@@ -1657,6 +1657,61 @@ int enqueue_route_send(const float* logits, int64_t T, int32_t E, int32_t k, int
 #undef MOE_FUSED
 }
 
+// Argument checks of the route + send part of the one-call entry points
+// (routing shape and groups, routing outputs, send outputs and workspace).
+int check_route_and_send(const float* logits, int64_t T, int32_t E, int32_t k, int32_t n_group,
+                         int32_t topk_group, int32_t R, const int32_t* topk_idx,
+                         const float* topk_w, const int32_t* counts, const int32_t* offsets,
+                         const int32_t* pair_row, const int32_t* row_token,
+                         const int32_t* rank_offsets, const void* workspace,
+                         size_t workspace_bytes) {
+  int st = check_route_shape(T, E, k);
+  if (st != MOE_OK) return st;
+  st = check_groups(E, k, n_group, topk_group);
+  if (st != MOE_OK) return st;
+  if (T > 0 && (!logits || !topk_idx || !topk_w)) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)))
+    return MOE_ERR_ALIGNMENT;
+  const size_t send_ws = workspace_bytes > kArrivalBytes ? workspace_bytes - kArrivalBytes : 0;
+  const char* ws = static_cast<const char*>(workspace);
+  return check_send(topk_idx, T, E, k, R, counts, offsets, pair_row, row_token, rank_offsets,
+                    ws ? ws + kArrivalBytes : nullptr, send_ws);
+}
+
+// Route + send of the one-call entry points, on the caller's zeroed workspace
+// (arrival counters, then the histogram matrix).  Small batches route and
+// send in one launch; otherwise the multi-block send reads the histogram
+// matrix, which the routing kernel fills itself when E is large enough (its
+// atomics then spread over enough addresses) and the histogram kernel
+// otherwise; the rank kernel's last block zeroes it again.
+int enqueue_route_and_send(const float* logits, int64_t T, int32_t E, int32_t k, int32_t n_group,
+                           int32_t topk_group, int32_t R, int32_t* topk_idx, float* topk_w,
+                           int32_t* counts, int32_t* offsets, int32_t* pair_row,
+                           int32_t* row_token, int32_t* rank_offsets, void* workspace,
+                           hipStream_t s) {
+  if (route_send_fusable(T, E, k))
+    return enqueue_route_send(logits, T, E, k, n_group, topk_group, R, topk_idx, topk_w,
+                              static_cast<uint32_t*>(workspace), counts, offsets, pair_row,
+                              row_token, rank_offsets, s);
+  const SendPlan plan = plan_send(T * k, E);
+  int st;
+  if (plan.fused) {  // single-block send: no histogram matrix
+    st = enqueue_route(logits, T, E, k, n_group, topk_group, topk_idx, topk_w, s);
+    if (st != MOE_OK) return st;
+    return enqueue_send(topk_idx, T, E, k, R, counts, offsets, pair_row, row_token, rank_offsets,
+                        nullptr, s);
+  }
+  int32_t* mat = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kArrivalBytes);
+  uint32_t* rank_arrivals = static_cast<uint32_t*>(workspace) + 1;
+  const bool count = E >= kRouteCountMinE;
+  st = enqueue_route(logits, T, E, k, n_group, topk_group, topk_idx, topk_w, s,
+                     count ? mat : nullptr, plan.chunk);
+  if (st == MOE_OK && !count) st = enqueue_send_hist(topk_idx, T, E, k, mat, s);
+  if (st != MOE_OK) return st;
+  return enqueue_send_ranks(topk_idx, T, E, k, R, counts, offsets, pair_row, row_token,
+                            rank_offsets, mat, rank_arrivals, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -1748,17 +1803,9 @@ int moe_route_dispatch(const float* logits, const void* x, int64_t T, int32_t E,
                        int32_t* expert_offsets, int32_t* pair_row, int32_t* row_token,
                        int32_t* rank_offsets, void* buf, int64_t capacity, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  int st = check_route_shape(T, E, k);
-  if (st != MOE_OK) return st;
-  st = check_groups(E, k, n_group, topk_group);
-  if (st != MOE_OK) return st;
-  if (T > 0 && (!logits || !topk_idx || !topk_w)) return MOE_ERR_INVALID_ARG;
-  if (T > 0 && (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)))
-    return MOE_ERR_ALIGNMENT;
-  const size_t send_ws = workspace_bytes > kArrivalBytes ? workspace_bytes - kArrivalBytes : 0;
-  char* ws = static_cast<char*>(workspace);
-  st = check_send(topk_idx, T, E, k, num_vranks, expert_counts, expert_offsets, pair_row,
-                  row_token, rank_offsets, ws ? ws + kArrivalBytes : nullptr, send_ws);
+  int st = check_route_and_send(logits, T, E, k, n_group, topk_group, num_vranks, topk_idx,
+                                topk_w, expert_counts, expert_offsets, pair_row, row_token,
+                                rank_offsets, workspace, workspace_bytes);
   if (st != MOE_OK) return st;
   st = check_rows(T, H, k, capacity, x, buf);
   if (st != MOE_OK || T == 0) return st;
@@ -1771,38 +1818,34 @@ int moe_route_dispatch(const float* logits, const void* x, int64_t T, int32_t E,
     return enqueue_send_recv(topk_idx, x, T, E, k, H, num_vranks, expert_counts, expert_offsets,
                              pair_row, row_token, rank_offsets, buf, capacity, s);
   }
-  if (route_send_fusable(T, E, k)) {
-    st = enqueue_route_send(logits, T, E, k, n_group, topk_group, num_vranks, topk_idx, topk_w,
-                            static_cast<uint32_t*>(workspace), expert_counts, expert_offsets,
-                            pair_row, row_token, rank_offsets, s);
-    if (st != MOE_OK) return st;
-    return enqueue_recv(x, pair_row, T, H, k, buf, capacity, s);
-  }
-  const SendPlan plan = plan_send(T * k, E);
-  if (plan.fused) {  // single-block send: no histogram matrix
-    st = enqueue_route(logits, T, E, k, n_group, topk_group, topk_idx, topk_w, s);
-    if (st == MOE_OK)
-      st = enqueue_send(topk_idx, T, E, k, num_vranks, expert_counts, expert_offsets, pair_row,
-                        row_token, rank_offsets, nullptr, s);
-    if (st != MOE_OK) return st;
-    return enqueue_recv(x, pair_row, T, H, k, buf, capacity, s);
-  }
-  // Multi-block send.  The histogram matrix in the workspace holds zeros
-  // between calls.  With enough experts the routing kernel counts the pairs
-  // into it (its atomics then spread over enough addresses); otherwise the
-  // histogram kernel fills it.  The rank kernel reads it, and its last block
-  // zeroes it again.
-  int32_t* mat = reinterpret_cast<int32_t*>(ws + kArrivalBytes);
-  uint32_t* rank_arrivals = static_cast<uint32_t*>(workspace) + 1;
-  const bool count = E >= kRouteCountMinE;
-  st = enqueue_route(logits, T, E, k, n_group, topk_group, topk_idx, topk_w, s,
-                     count ? mat : nullptr, plan.chunk);
-  if (st == MOE_OK && !count) st = enqueue_send_hist(topk_idx, T, E, k, mat, s);
-  if (st == MOE_OK)
-    st = enqueue_send_ranks(topk_idx, T, E, k, num_vranks, expert_counts, expert_offsets, pair_row,
-                            row_token, rank_offsets, mat, rank_arrivals, s);
+  st = enqueue_route_and_send(logits, T, E, k, n_group, topk_group, num_vranks, topk_idx, topk_w,
+                              expert_counts, expert_offsets, pair_row, row_token, rank_offsets,
+                              workspace, s);
   if (st != MOE_OK) return st;
   return enqueue_recv(x, pair_row, T, H, k, buf, capacity, s);
+}
+
+int moe_route_dispatch_fp8(const float* logits, const void* x, int64_t T, int32_t E, int32_t k,
+                           int32_t n_group, int32_t topk_group, int32_t H, int32_t num_vranks,
+                           int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
+                           int32_t* expert_offsets, int32_t* pair_row, int32_t* row_token,
+                           int32_t* rank_offsets, void* buf_q, float* buf_scale,
+                           int64_t capacity, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  int st = check_route_and_send(logits, T, E, k, n_group, topk_group, num_vranks, topk_idx,
+                                topk_w, expert_counts, expert_offsets, pair_row, row_token,
+                                rank_offsets, workspace, workspace_bytes);
+  if (st != MOE_OK) return st;
+  st = check_fp8_rows(T, H, k, capacity, x, buf_q, buf_scale);
+  if (st != MOE_OK || T == 0) return st;
+  if (workspace == nullptr || workspace_bytes < kArrivalBytes) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, 4)) return MOE_ERR_ALIGNMENT;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = enqueue_route_and_send(logits, T, E, k, n_group, topk_group, num_vranks, topk_idx, topk_w,
+                              expert_counts, expert_offsets, pair_row, row_token, rank_offsets,
+                              workspace, s);
+  if (st != MOE_OK) return st;
+  return enqueue_recv_fp8(x, pair_row, T, H, k, buf_q, buf_scale, capacity, s);
 }
 
 int moe_dispatch_recv_fp8(const void* x, const int32_t* pair_row, int64_t T, int32_t H, int32_t k,

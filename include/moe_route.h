@@ -278,6 +278,28 @@ int moe_dispatch_fp8(const int32_t* topk_idx, const void* x, int64_t T,
                      void* stream);
 
 /*
+ * moe_route_dispatch_fp8 - moe_route_dispatch with the block-scaled fp8
+ * receive of moe_dispatch_recv_fp8: the router's top-K output goes straight
+ * into dispatch, and the rows travel as E4M3 codes plus one fp32 scale per
+ * 128 elements ("Lower latency and higher throughput with multi-node
+ * DeepSeek deployment", sections "MoE Router" and "Quantization").
+ * Arguments are moe_route_dispatch's, with buf_q / buf_scale as in
+ * moe_dispatch_recv_fp8 in place of buf; the same workspace rules apply
+ * (moe_route_dispatch_workspace_bytes, zeroed once, left zeroed).  All
+ * arguments are checked before anything is enqueued.  The outputs equal
+ * moe_route_topk_grouped followed by moe_dispatch_fp8.
+ * Errors: as moe_route_dispatch and moe_dispatch_recv_fp8.
+ */
+int moe_route_dispatch_fp8(const float* logits, const void* x, int64_t T, int32_t E,
+                           int32_t k, int32_t n_group, int32_t topk_group,
+                           int32_t H, int32_t num_vranks,
+                           int32_t* topk_idx, float* topk_w,
+                           int32_t* expert_counts, int32_t* expert_offsets,
+                           int32_t* pair_row, int32_t* row_token, int32_t* rank_offsets,
+                           void* buf_q, float* buf_scale, int64_t capacity,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * moe_combine - receiver-side weighted sum of each token's k expert-output
  * rows ("Efficient and portable mixture-of-experts communication", section
  * "Combine"; accumulation at the receiver as in "Enabling trillion-parameter

@@ -230,3 +230,32 @@ def test_route_dispatch_checks_every_part_before_enqueueing(lib):
     assert call(a2=128, a17=1024, a19=256, a18=P16 + 2) == ALIGN
     assert call(a2=0, a0=None, a1=None, a9=None, a10=None, a11=None, a12=None, a13=None,
                 a14=None, a16=None, a17=0, a18=None, a19=0) == OK
+
+
+def test_route_dispatch_fp8_checks_every_part_before_enqueueing(lib):
+    f = lib.moe_route_dispatch_fp8
+    ws = lib.moe_route_dispatch_workspace_bytes(8192, 256, 8)
+    # logits, x, T, E, k, n_group, topk_group, H, R, idx, w, counts, offsets, pair_row,
+    # row_token, rank, buf_q, buf_scale, cap, ws, wsb
+    base = [P16, P16, 8192, 256, 8, 1, 1, 7168, 32, P16, P16, P16, P16, P16, P16, None, P16, P16,
+            8192 * 8, P16, ws, S]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a4=33) == INVALID                  # k > 32 (routing)
+    assert call(a5=3) == INVALID                   # E % n_group != 0
+    assert call(a0=None) == INVALID                # null logits
+    assert call(a8=5) == INVALID                   # E % R != 0 (send)
+    assert call(a18=8192 * 8 - 1) == CAP           # capacity < T*k (recv)
+    assert call(a7=7176) == ALIGN                  # H % 128 != 0 (fp8 blocks)
+    assert call(a7=7170) == ALIGN                  # H % 8 != 0
+    assert call(a17=None) == INVALID               # null scales
+    assert call(a16=P16 + 8) == ALIGN              # codes not 16-byte aligned
+    assert call(a19=None) == WS                    # no workspace
+    assert call(a20=ws - 1) == WS                  # short workspace
+    assert call(a2=0, a0=None, a1=None, a9=None, a10=None, a11=None, a12=None, a13=None,
+                a14=None, a16=None, a17=None, a18=0, a19=None, a20=0) == OK

@@ -86,3 +86,46 @@ def test_fp8_chain_matches_oracle():
     rq, rs = oracle.dispatch_rows_fp8(wl.x, pr, cfg.P)
     assert np.array_equal(host(bs).view(np.uint32), rs.view(np.uint32))
     assert np.array_equal(host(bq), rq)
+
+
+@pytest.mark.parametrize("T,E,k,R,H,G,TG", [
+    (16, 8, 2, 1, 256, 1, 1),          # one launch for route + send
+    (128, 256, 8, 32, 7168, 1, 1),     # DSv3 decode shape
+    (300, 384, 8, 48, 1024, 8, 4),     # group-limited, 16-wave single-block send
+    (3000, 64, 4, 8, 512, 1, 1),       # lane-group routing, histogram kernel (E < 128)
+    (4096, 256, 8, 32, 2048, 1, 1),    # routing that counts the send histogram
+])
+def test_route_dispatch_fp8_matches_the_separate_calls(T, E, k, R, H, G, TG):
+    """moe_route_dispatch_fp8 against routing then moe_dispatch_fp8: indices
+    and weights, every send output, codes and scales bit-identical; the
+    codes also against the oracle on the oracle's routing; the workspace is
+    zero after two calls."""
+    import combine_topk_route_amd as m
+
+    print(f"[fp8] route_dispatch_fp8 T={T} E={E} k={k} H={H} groups {TG}/{G}", flush=True)
+    rng = np.random.default_rng(T + E + H)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    x = workloads.bf16_from_f32(rng.standard_normal((T, H)).astype(np.float32))
+    lg, xd = torch.from_numpy(logits).to(DEV), dev_bf16(x)
+    ws = torch.zeros((m.moe_route_dispatch_workspace_bytes(T, E, k),), dtype=torch.uint8,
+                     device=DEV)
+    for _ in range(2):
+        idx, w, send, q, s = m.moe_route_dispatch_fp8(lg, xd, k, R, n_group=G, topk_group=TG,
+                                                      workspace=ws)
+    if TG < G:
+        idx2, w2 = m.moe_route_topk_grouped(lg, k, G, TG)
+    else:
+        idx2, w2 = m.moe_route_topk(lg, k)
+    send2, q2, s2 = m.moe_dispatch_fp8(idx2, xd, E, R)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(w.view(torch.int32), w2.view(torch.int32))
+    for a, b in zip(send, send2):
+        assert torch.equal(a, b)
+    assert torch.equal(q, q2) and torch.equal(s.view(torch.int32), s2.view(torch.int32))
+    assert int(ws.count_nonzero().item()) == 0
+    r_idx = (oracle.route_topk_grouped(logits, k, G, TG) if TG < G else oracle.route_topk(logits, k))[0]
+    assert np.array_equal(host(idx), r_idx)
+    pr, _ = oracle.dispatch_slots(r_idx, E)
+    rq, rs = oracle.dispatch_rows_fp8(x, pr, T * k)
+    assert np.array_equal(host(q), rq)
+    assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32))
