@@ -123,6 +123,24 @@ class MoeBuffers:
                             stream=stream)
         return s, self.buf_q[: T * self.k], self.buf_scale[: T * self.k]
 
+    def route_dispatch_fp8(self, logits: torch.Tensor, x: torch.Tensor, n_group: int = 1,
+                           topk_group: int = 1, stream=None):
+        """Route + send + fp8 receive in one call; returns (topk_idx, topk_w,
+        SendResult, codes [T*k, H], scales [T*k, H/128])."""
+        if self.buf_q is None:
+            raise ValueError("constructed without fp8=True")
+        T = x.shape[0]
+        v = self._v(T)
+        s = v.send
+        q, sc = self.buf_q[: T * self.k], self.buf_scale[: T * self.k]
+        _b.moe_route_dispatch_fp8(logits, x, self.k, self.R, n_group=n_group,
+                                  topk_group=topk_group, topk_idx=v.topk_idx, topk_w=v.topk_w,
+                                  buf_q=q, buf_scale=sc, expert_counts=s.expert_counts,
+                                  expert_offsets=s.expert_offsets, pair_row=s.pair_row,
+                                  row_token=s.row_token, rank_offsets=s.rank_offsets,
+                                  workspace=self.route_workspace, stream=stream)
+        return v.topk_idx, v.topk_w, s, q, sc
+
     def combine(self, y: torch.Tensor, pair_row: torch.Tensor, topk_w: torch.Tensor,
                 stream=None) -> torch.Tensor:
         v = self._v(pair_row.shape[0])

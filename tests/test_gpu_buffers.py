@@ -39,6 +39,22 @@ def test_buffers_match_plain_calls_and_do_not_allocate():
         assert np.array_equal(host_bf16(buf), host_bf16(r_buf))
         assert np.array_equal(host_bf16(out), host_bf16(r_out))
         assert torch.equal(q, r_q) and torch.equal(sc, r_sc)
+        # The one-call forms (combine on the object's own routing views takes
+        # the path that checks only y) allocate nothing either.
+        torch.cuda.synchronize()
+        before = torch.cuda.memory_allocated()
+        idx2, w2, send2, buf2 = mb.route_dispatch(logits, x)
+        out2 = mb.combine(y, send2.pair_row, w2)
+        i8, w8, s8b, q2, sc2 = mb.route_dispatch_fp8(logits, x)
+        torch.cuda.synchronize()
+        assert torch.cuda.memory_allocated() == before
+        assert torch.equal(idx2, r_idx) and torch.equal(w2, r_w)
+        for a, b in zip(send2, r_send):
+            assert torch.equal(a, b)
+        assert np.array_equal(host_bf16(buf2), host_bf16(r_buf))
+        assert np.array_equal(host_bf16(out2), host_bf16(r_out))
+        assert torch.equal(i8, r_idx) and torch.equal(q2, r_q) and torch.equal(sc2, r_sc)
+        assert int(mb.route_workspace.count_nonzero().item()) == 0
     with pytest.raises(ValueError):
         mb.route(torch.zeros((cfg.T + 1, cfg.E), device="cuda"))
 
