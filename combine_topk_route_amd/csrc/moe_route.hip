@@ -931,7 +931,7 @@ __device__ __forceinline__ void send_rank_block(
       }
     }
   }
-  if (!FUSED && clear_mat) {  // every block has staged the matrix: zero it for the next call
+  if (!FUSED && clear_mat) {  // every block has read the matrix: zero it for the next call
     for (int i = threadIdx.x; i < nb * E; i += THREADS) ws_cnt[i] = 0;
     if (threadIdx.x == 0) __hip_atomic_store(arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
