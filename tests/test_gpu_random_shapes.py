@@ -104,3 +104,38 @@ def test_random_shape_through_the_one_call_path(case, workspace):
     assert np.array_equal(buf_bits, oracle.dispatch_rows(x, pr, T * k))
     w32 = host(w).astype(np.float32)
     assert np.array_equal(host_bf16(out), oracle.combine(buf_bits, pr, w32))
+
+
+FP8_CASES = CASES[::3]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=[
+    f"T{c[0]}-E{c[1]}-k{c[2]}-R{c[3]}-g{c[5]}.{c[6]}" for c in FP8_CASES])
+def test_random_shape_through_the_fp8_one_call_path(case, workspace):
+    """moe_route_dispatch_fp8 on every third shape (rows widened to a
+    multiple of 128): indices, slots, E4M3 codes and fp32 scales bit-exact
+    against the oracle; the shared workspace is zero after each call."""
+    import combine_topk_route_amd as m
+
+    T, E, k, R, H, G, TG = case
+    H = 128 * max(1, -(-H // 128))
+    print(f"\n[random fp8] T={T} E={E} k={k} R={R} H={H} groups {TG}/{G}", flush=True)
+    rng = np.random.default_rng(T * 17 + E * 5 + k)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    x = workloads.bf16_from_f32(rng.standard_normal((T, H)).astype(np.float32))
+    idx, w, send, q, s = m.moe_route_dispatch_fp8(dev_f32(logits), dev_bf16(x), k, R,
+                                                  n_group=G, topk_group=TG, workspace=workspace)
+    torch.cuda.synchronize()
+    assert int(workspace.count_nonzero().item()) == 0
+    if TG < G:
+        r_idx, r_w, _ = oracle.route_topk_grouped(logits, k, G, TG)
+    else:
+        r_idx, r_w, _ = oracle.route_topk(logits, k)
+    assert np.array_equal(host(idx), r_idx)
+    assert_weights_close(host(w), r_w)
+    pr, rt = oracle.dispatch_slots(r_idx, E)
+    assert np.array_equal(host(send.pair_row), pr)
+    assert np.array_equal(host(send.row_token), rt)
+    rq, rs = oracle.dispatch_rows_fp8(x, pr, T * k)
+    assert np.array_equal(host(q), rq)
+    assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32))
