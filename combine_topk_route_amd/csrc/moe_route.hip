@@ -248,10 +248,13 @@ constexpr int kRouteCountMinE = 128;
 
 // Softmax numerator exp(a - m).  The difference is split into its fp32
 // rounding d and the exact remainder r (TwoSum), and exp(d + r) is taken as
-// exp(d) * (1 + r): the subtraction then adds no error of its own.
+// exp(d) * (1 + r): the subtraction then adds no error of its own.  A
+// difference beyond the fp32 range (finite logits more than FLT_MAX apart)
+// is held at -FLT_MAX: exp gives 0 and r stays finite, where -inf would make
+// r, and the whole softmax, NaN.
 __device__ __forceinline__ float shifted_exp(float a, float m) {
   const float b = -m;
-  const float d = a + b;
+  const float d = fmaxf(a + b, -__FLT_MAX__);
   const float bb = d - a;
   const float r = (a - (d - bb)) + (b - bb);
   const float ed = expf(d);

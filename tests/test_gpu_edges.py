@@ -125,6 +125,27 @@ def test_route_wide_logit_range():
     _route_check(logits, 8)
 
 
+def test_route_logits_further_apart_than_the_fp32_range():
+    """Finite logits whose differences overflow fp32 (the winners' weights
+    then include exact zeros): weights stay finite and match the float64
+    oracle; indices are exact.  Both routing kernels (as given and tiled)."""
+    rng = np.random.default_rng(6)
+    fmax = np.float32(3.4e38)
+    logits = rng.standard_normal((64, 256)).astype(np.float32)
+    logits[0, 3], logits[0, 200] = fmax, -fmax            # k-th winner far below the first
+    logits[1, :] = -fmax
+    logits[1, 17] = fmax                                  # every other expert overflows
+    logits[2, :8] = np.float32(2e38)
+    logits[2, 8:] = np.float32(-2e38)                     # eight equal winners, the rest at -2e38
+    logits[3, ::2] = np.float32(1e38)
+    logits[3, 1::2] = np.float32(-3e38)
+    logits[4, 5] = np.float32(3.3e38)
+    logits[4, 6] = np.float32(-1e38)                      # 4.3e38 below the first
+    idx, w = _route_check(logits, 8)
+    assert np.all(np.isfinite(w))
+    assert w[1, 0] == 1.0 and np.all(w[1, 1:] == 0.0)
+
+
 # ------------------------------------------------------------------ dispatch send
 
 def _send_check(idx, E, R):

@@ -71,6 +71,23 @@ def test_route_closed_forms():
     assert math.isclose(w[1, 1], math.exp(-1.0) / (1.0 + math.exp(-1.0)), rel_tol=1e-14)
 
 
+def test_route_closed_forms_past_the_fp32_range():
+    # logits further apart than FLT_MAX: e^(a - m) underflows to exactly 0 in
+    # float64, so the top logit takes weight 1, and equal winners split it
+    fmax = float(np.finfo(np.float32).max)
+    logits = np.full((3, 8), -fmax, np.float32)
+    logits[0, 5] = fmax
+    logits[1, 2] = logits[1, 6] = np.float32(2e38)
+    logits[1, [0, 1, 3]] = np.float32(-2e38)
+    logits[2, :] = np.float32(-3e38)
+    logits[2, 4] = np.float32(1e38)
+    logits[2, 1] = np.float32(0.5)
+    idx, w, w32 = oracle.route_topk(logits, 3)
+    assert idx.tolist() == [[5, 0, 1], [2, 6, 0], [4, 1, 0]]
+    assert w[0].tolist() == [1.0, 0.0, 0.0] and w[1].tolist() == [0.5, 0.5, 0.0]
+    assert w[2].tolist() == [1.0, 0.0, 0.0] and np.all(np.isfinite(w32))
+
+
 def test_route_invariants_on_all_configs():
     for name, cfg in workloads.CONFIGS.items():
         T = min(cfg.T, 1024)
