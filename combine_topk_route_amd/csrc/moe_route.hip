@@ -241,6 +241,7 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kRouteWavesPerBlock = 4;
 constexpr int kRouteThreads = kRouteWavesPerBlock * kWave;
 constexpr int64_t kRouteWaveMaxTokens = 2048;  // up to here plain routing uses one wave per token
+constexpr int64_t kRouteMaxBlocks = int64_t(1) << 20;  // beyond this, waves loop over token tiles
 // Fewest experts for which moe_route_dispatch's routing kernel counts the send
 // histogram itself: with fewer, its per-pair atomics pile onto too few
 // addresses (E = 8: each takes a few hundred).
@@ -379,18 +380,18 @@ __device__ __forceinline__ void cache_push(uint32_t kv, int i, uint32_t (&h)[C],
 // COUNT: the owner of winner j also adds the pair p = t*k + j to the send
 // histogram matrix, row p / chunk (chunk >= 64 > j, so a token's pairs span at
 // most two rows); the matrix must hold zeros beforehand.
+// The calling wave routes tokens t_wave .. t_wave + 64/G - 1 (t_wave < T).
 template <int G, int IPL, bool VEC, bool COUNT>
-__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
-    const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, int32_t* __restrict__ hist_mat, uint32_t chunk) {
+__device__ __forceinline__ void route_topk_tile(const float* __restrict__ logits, int64_t T,
+                                                int E, int k, int32_t* __restrict__ topk_idx,
+                                                float* __restrict__ topk_w,
+                                                int32_t* __restrict__ hist_mat, uint32_t chunk,
+                                                int64_t t_wave) {
   constexpr int TPW = kWave / G;         // tokens per wave
   constexpr int C = IPL < 4 ? IPL : 4;   // cached candidates per lane
   const int lane = lane_id();
-  const int wv = threadIdx.x / kWave;
   const int q = lane / G;  // token slot inside the wave
   const int g = lane % G;  // lane inside the token's group
-  const int64_t t_wave = (int64_t(blockIdx.x) * kRouteWavesPerBlock + wv) * TPW;
-  if (t_wave >= T) return;  // whole waves leave; no block barrier follows
   const int64_t t = t_wave + q;
   const int64_t t_ld = t < T ? t : T - 1;  // lanes past T repeat the last token and store nothing
   const int e0 = g * IPL;
@@ -512,6 +513,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     const float psel = (zsum + zcomp) / s;   // the winners' total probability
     topk_w[t * k + g] = p / psel;            // renormalised to sum to 1
   }
+}
+
+// Waves take tiles of 64/G tokens in grid-stride order, so the grid stays
+// within the launch's 32-bit work-item count at any T.  No block barrier
+// follows the loop: a wave past T just leaves.
+template <int G, int IPL, bool VEC, bool COUNT>
+__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
+    const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, int32_t* __restrict__ hist_mat, uint32_t chunk) {
+  constexpr int TPW = kWave / G;  // tokens per wave
+  const int64_t stride = int64_t(gridDim.x) * kRouteWavesPerBlock * TPW;
+  for (int64_t t_wave = (int64_t(blockIdx.x) * kRouteWavesPerBlock + threadIdx.x / kWave) * TPW;
+       t_wave < T; t_wave += stride)
+    route_topk_tile<G, IPL, VEC, COUNT>(logits, T, E, k, topk_idx, topk_w, hist_mat, chunk,
+                                        t_wave);
 }
 
 // One wave per token; IPL logits per lane (expert e = lane + 64 * i).  The
@@ -638,10 +654,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_wave_kernel(
     const float* __restrict__ logits, int64_t T, int E, int k, int n_group, int topk_group,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ hist_mat,
     uint32_t chunk) {
-  const int64_t t = int64_t(blockIdx.x) * kRouteWavesPerBlock + threadIdx.x / kWave;
-  if (t >= T) return;  // whole waves leave; no block barrier follows
-  route_wave_token<IPL, GROUPED, COUNT>(logits, t, E, k, n_group, topk_group, topk_idx, topk_w,
-                                        hist_mat, chunk);
+  // Grid-stride over tokens, as in route_topk_kernel; no block barrier follows.
+  const int64_t stride = int64_t(gridDim.x) * kRouteWavesPerBlock;
+  for (int64_t t = int64_t(blockIdx.x) * kRouteWavesPerBlock + threadIdx.x / kWave; t < T;
+       t += stride)
+    route_wave_token<IPL, GROUPED, COUNT>(logits, t, E, k, n_group, topk_group, topk_idx, topk_w,
+                                          hist_mat, chunk);
 }
 
 // ---------------------------------------------------------------------------
@@ -1358,6 +1376,9 @@ template <typename... KArgs, typename... Args>
 int launch(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t st,
            Args... args) {
   static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel arity");
+  // The dispatch packet holds the grid as 32-bit work-item counts; every
+  // plan caps its grid well below that, and this keeps it so.
+  if (uint64_t(grid.x) * block.x > 0xFFFFFFFFull) return MOE_ERR_INVALID_ARG;
   std::tuple<KArgs...> packed(static_cast<KArgs>(args)...);
   void* argv[sizeof...(KArgs)];
   arg_ptrs(packed, argv, std::index_sequence_for<KArgs...>{});
@@ -1414,7 +1435,8 @@ int enqueue_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t 
   const bool count = hist_mat != nullptr;
   const uint32_t ch = uint32_t(chunk);
   if (grouped || T <= kRouteWaveMaxTokens) {
-    const dim3 grid(unsigned((T + kRouteWavesPerBlock - 1) / kRouteWavesPerBlock));
+    const int64_t nb = (T + kRouteWavesPerBlock - 1) / kRouteWavesPerBlock;
+    const dim3 grid(unsigned(nb < kRouteMaxBlocks ? nb : kRouteMaxBlocks));
     const int ipl = (E + kWave - 1) / kWave;
     const int ng = grouped ? n_group : 1, tg = grouped ? topk_group : 1;
 #define MOE_ROUTE_GC(IPL_, GR_)                                                              \
@@ -1437,7 +1459,8 @@ int enqueue_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t 
   }
   const RoutePlan p = plan_route(T, E, k);
   const int64_t tokens_per_block = int64_t(kRouteWavesPerBlock) * (kWave / p.G);
-  const dim3 grid(unsigned((T + tokens_per_block - 1) / tokens_per_block));
+  const int64_t nb = (T + tokens_per_block - 1) / tokens_per_block;
+  const dim3 grid(unsigned(nb < kRouteMaxBlocks ? nb : kRouteMaxBlocks));
   const bool vec = p.IPL % 4 == 0 && E % 4 == 0 && aligned(logits, 16);
 #define MOE_ROUTE_VC(G_, IPL_, VEC_)                                                            \
   return count ? launch(route_topk_kernel<G_, IPL_, VEC_, true>, grid, block, 0, s, logits, T, \
