@@ -4,6 +4,8 @@
   Routing runs far past 2^32 lanes, so the routing kernel's waves loop over
   token tiles; send runs 64 blocks of 2^25 pairs; recv and combine run
   2^30 row units through their capped grids.
+* The one-call path (route, send, recv) at T*k = 2^31 - 32 with E = 128,
+  where the routing kernel counts the send histogram.
 * Group-limited routing with 64*T past 2^32 (one wave per token, looping).
 * Row offsets past 2^31 16-byte units (H = 8192, T = 2^21 + 3): recv,
   combine and the fp8 recv address bytes beyond 2^35.
@@ -109,18 +111,22 @@ def _check_slots(idx_flat, E, k, send):
     off = torch.zeros(E + 1, dtype=torch.int64, device=DEV)
     off[1:] = torch.cumsum(counts, 0)
     assert torch.equal(send.expert_offsets.long(), off)
-    seen = off[:E].clone()
+    seen = off[:E].clone()  # expert e's next row
     pr = send.pair_row.view(-1)
+    experts = torch.arange(E, device=DEV)
     for p0 in range(0, P, EL):
         e_c = idx_flat[p0:p0 + EL].long()
         pr_c = pr[p0:p0 + EL].long()
+        n = e_c.numel()
+        # a stable sort keeps each expert's pairs in ascending p; a pair's
+        # rank among its expert's pairs in this chunk is its sorted position
+        # minus the expert's first sorted position
+        sorted_e, order = torch.sort(e_c, stable=True)
+        first = torch.searchsorted(sorted_e, experts)
         want = torch.empty_like(pr_c)
-        for e in range(E):
-            m = e_c == e
-            rank = torch.cumsum(m, 0, dtype=torch.int64) - 1
-            want = torch.where(m, seen[e] + rank, want)
-            seen[e] += m.sum()
-        assert torch.equal(pr_c, want), f"pair rows differ in pairs [{p0}, {p0 + pr_c.numel()})"
+        want[order] = seen[sorted_e] + torch.arange(n, device=DEV) - first[sorted_e]
+        seen += torch.bincount(e_c, minlength=E)
+        assert torch.equal(pr_c, want), f"pair rows differ in pairs [{p0}, {p0 + n})"
         tok = torch.arange(p0, p0 + pr_c.numel(), device=DEV) // k
         assert torch.equal(send.row_token[pr_c].long(), tok), "row_token differs"
     assert torch.equal(seen, off[1:])
@@ -189,6 +195,40 @@ def test_pairs_at_the_int32_limit():
     for t0 in range(0, T, n):
         assert not bool((out[t0:t0 + n].view(torch.int16) == -1).all(1).any()), \
             f"a token in [{t0}, {t0 + n}) was not combined"
+
+
+def test_one_call_path_at_the_pair_limit():
+    """moe_route_dispatch with T*k = 2^31 - 32 and E = 128: the routing kernel
+    counts the send histogram itself (rows of 2^25 pairs), the rank kernel
+    reads and clears it; the workspace is zero again afterwards."""
+    import combine_topk_route_amd as m
+
+    T, E, k, R, H = (1 << 26) - 1, 128, 32, 32, 8
+    _say(f"route_dispatch T={T} E={E} k={k} R={R} H={H}")
+    g = torch.Generator(device=DEV).manual_seed(32)
+    logits = _randn((T, E), g)
+    x = _randn((T, H), g, torch.bfloat16)
+    ws = torch.zeros((m.moe_route_dispatch_workspace_bytes(T, E, k),), dtype=torch.uint8,
+                     device=DEV)
+    idx = _full((T, k), -1, torch.int32)
+    w = _full((T, k), float("nan"), torch.float32)
+    idx, w, send, buf = m.moe_route_dispatch(logits, x, k, R, topk_idx=idx, topk_w=w,
+                                             workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero().item()) == 0
+    n = _step(E)
+    for t0 in range(0, T, n):
+        _check_topk_rows(logits[t0:t0 + n], idx[t0:t0 + n])
+        assert bool(torch.isfinite(w[t0:t0 + n]).all())
+    s = _sample(T, 2048, 4)
+    st = torch.from_numpy(s).to(DEV)
+    r_idx, r_w, _ = oracle.route_topk(host(logits[st]), k)
+    assert np.array_equal(host(idx[st]), r_idx)
+    assert_weights_close(host(w[st]), r_w)
+    del logits
+    _check_slots(idx.view(-1), E, k, send)
+    assert torch.equal(send.rank_offsets.long(), send.expert_offsets.long()[::E // R])
+    _check_rows(buf, x, send.row_token)
 
 
 def test_grouped_routing_past_the_32_bit_grid():
