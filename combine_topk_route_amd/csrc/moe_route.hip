@@ -12,11 +12,13 @@
 //
 //   route_topk_kernel    batches above 2048 tokens: 16, 32 or 64 lanes per
 //                        token (the fewest that still fill the chip), each
-//                        lane holding consecutive experts: fp32 softmax over
-//                        the E logits held in registers; every lane caches
+//                        lane holding consecutive experts; every lane caches
 //                        its 4 best order-preserving 32-bit keys, so each of
 //                        the k selection rounds is one DPP maximum over the
-//                        cache heads of the token's lanes.  Inside
+//                        cache heads of the token's lanes.  The weights are
+//                        the winners' softmax probabilities renormalised
+//                        over the k winners, formed from their k numerators
+//                        alone (the E-term denominator cancels).  Inside
 //                        moe_route_dispatch (E >= 128) the routing kernels
 //                        also count each pair into the send histogram with
 //                        an atomic add, in place of send_hist_kernel.
@@ -123,22 +125,7 @@ __device__ __forceinline__ uint32_t readlane(uint32_t v, int lane) {
 // two broadcasts fold rows into lane 63, which is read into a scalar.  The
 // `old` operand of each DPP move is the operation's identity (lanes a row
 // mask leaves out then contribute nothing), which lets the compiler fuse the
-// move into the arithmetic: one v_max_u32_dpp / v_add_f32_dpp per step.
-
-// Fixed association order, so the sum is the same on every run (operands
-// here are non-negative, so +0.0 is an exact identity).
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#define MOE_STEP(CTRL, RM) v += __uint_as_float(dpp<CTRL, RM>(0u, __float_as_uint(v)))
-  MOE_STEP(kDppQuad1032, 0xF);
-  MOE_STEP(kDppQuad2301, 0xF);
-  MOE_STEP(kDppRowHalfMirror, 0xF);
-  MOE_STEP(kDppRowMirror, 0xF);
-  MOE_STEP(kDppRowBcast15, 0xA);
-  MOE_STEP(kDppRowBcast31, 0xC);
-#undef MOE_STEP
-  return __uint_as_float(readlane(__float_as_uint(v), kWave - 1));
-}
-
+// move into the arithmetic: one v_max_u32_dpp per step.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #define MOE_STEP(CTRL, RM) v = max(v, dpp<CTRL, RM>(0u, v))
   MOE_STEP(kDppQuad1032, 0xF);
@@ -262,10 +249,8 @@ __device__ __forceinline__ float shifted_exp(float a, float m) {
   return __builtin_fmaf(ed, r, ed);
 }
 
-// Reductions over the G lanes that share one token (G = 16, 32 or 64; a
-// group starts at a multiple of G).  Every lane of the group gets the result.
-// The four in-row steps are butterflies, so each lane adds the same operands
-// in the same pairs: the sum is bit-identical across the group.
+// Maximum over the G lanes that share one token (G = 16, 32 or 64; a group
+// starts at a multiple of G).  Every lane of the group gets the result.
 template <int G>
 __device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
   v = max(v, dpp<kDppQuad1032, 0xF>(0u, v));
@@ -281,27 +266,6 @@ __device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
     v = max(v, dpp<kDppRowBcast31, 0xC>(0u, v));
     v = readlane(v, kWave - 1);
   }
-  return v;
-}
-
-template <int G>
-__device__ __forceinline__ float group_sum_f32(float v) {
-#define MOE_STEP(CTRL, RM) v += __uint_as_float(dpp<CTRL, RM>(0u, __float_as_uint(v)))
-  MOE_STEP(kDppQuad1032, 0xF);
-  MOE_STEP(kDppQuad2301, 0xF);
-  MOE_STEP(kDppRowHalfMirror, 0xF);
-  MOE_STEP(kDppRowMirror, 0xF);
-  if constexpr (G == 32) {
-    MOE_STEP(kDppRowBcast15, 0xA);
-    const uint32_t lo = readlane(__float_as_uint(v), 31);
-    const uint32_t hi = readlane(__float_as_uint(v), kWave - 1);
-    v = __uint_as_float(lane_id() < 32 ? lo : hi);
-  } else if constexpr (G == 64) {
-    MOE_STEP(kDppRowBcast15, 0xA);
-    MOE_STEP(kDppRowBcast31, 0xC);
-    v = __uint_as_float(readlane(__float_as_uint(v), kWave - 1));
-  }
-#undef MOE_STEP
   return v;
 }
 
@@ -422,25 +386,8 @@ __device__ __forceinline__ void route_topk_tile(const float* __restrict__ logits
 
   // Order keys (0 marks "no expert"); the maximum logit is the maximum key.
   uint32_t key[IPL];
-  uint32_t kmax = 0u;
 #pragma unroll
-  for (int i = 0; i < IPL; ++i) {
-    key[i] = e0 + i < E ? order_key(lv[i]) : 0u;
-    kmax = max(kmax, key[i]);
-  }
-  const float m = key_value(group_max_u32<G>(kmax));
-
-  // Softmax denominator over all E experts: lane-local sum in item order,
-  // then the group's butterfly.
-  // (Lanes past E hold 0.0, a finite stand-in whose term is dropped by a
-  // select, so the loop has no branches.)
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < IPL; ++i) {
-    const float z = shifted_exp(lv[i], m);
-    s += e0 + i < E ? z : 0.f;
-  }
-  s = group_sum_f32<G>(s);
+  for (int i = 0; i < IPL; ++i) key[i] = e0 + i < E ? order_key(lv[i]) : 0u;
 
   uint32_t h[C];
   int hi[C];
@@ -454,8 +401,10 @@ __device__ __forceinline__ void route_topk_tile(const float* __restrict__ logits
   int rem = E - e0 < IPL ? (E - e0 > 0 ? E - e0 : 0) : IPL;  // candidates not yet taken
 
   uint32_t my_key = 0u;  // lane g < k: key of winner j = g
+  uint32_t top = 0u;     // the first winner's key: the token's largest logit
   for (int j = 0; j < k; ++j) {
     const uint32_t best = group_max_u32<G>(h[0]);
+    top = max(top, best);  // winners come in descending order: the first one
     const bool hit = h[0] == best;
     const uint64_t hits = ballot(hit);
     bool owner = hit;
@@ -501,18 +450,16 @@ __device__ __forceinline__ void route_topk_tile(const float* __restrict__ logits
     }
   }
 
-  // Lane g < k of each token: numerator of winner g; the winners' total by a
-  // compensated sum over the group; the renormalised probability.  Only the
-  // k winners are divided by the softmax denominator.
+  // Lane g < k of each token: numerator of winner g against the largest
+  // logit; the winners' total by a compensated sum over the group; winner
+  // g's share of it.  That share is its softmax probability renormalised
+  // over the k winners: the softmax denominator cancels, so it is never
+  // formed.
   float z = 0.f;
-  if (g < k) z = shifted_exp(key_value(my_key), m);
+  if (g < k) z = shifted_exp(key_value(my_key), key_value(top));
   float zsum = z, zcomp = 0.f;
   group_sum_compensated<G>(zsum, zcomp);
-  if (g < k && t < T) {
-    const float p = z / s;                   // softmax probability of winner g
-    const float psel = (zsum + zcomp) / s;   // the winners' total probability
-    topk_w[t * k + g] = p / psel;            // renormalised to sum to 1
-  }
+  if (g < k && t < T) topk_w[t * k + g] = z / (zsum + zcomp);
 }
 
 // Waves take tiles of 64/G tokens in grid-stride order, so the grid stays
@@ -547,27 +494,12 @@ __device__ __forceinline__ void route_wave_token(const float* __restrict__ logit
   const int lane = lane_id();
   const float* row = logits + t * E;
 
-  float lv[IPL];
-  uint32_t key[IPL];
-  uint32_t kmax = 0u;
+  uint32_t key[IPL];  // order keys; 0 marks "no expert"
 #pragma unroll
   for (int i = 0; i < IPL; ++i) {
     const int e = lane + i * kWave;
-    lv[i] = e < E ? row[e] : 0.f;
-    key[i] = e < E ? order_key(lv[i]) : 0u;
-    kmax = max(kmax, key[i]);
+    key[i] = e < E ? order_key(row[e]) : 0u;
   }
-  const float m = key_value(wave_max_u32(kmax));
-
-  float zv[IPL];  // softmax numerators
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < IPL; ++i) {
-    const int e = lane + i * kWave;
-    zv[i] = e < E ? shifted_exp(lv[i], m) : 0.f;
-    s += zv[i];
-  }
-  s = wave_sum_f32(s);  // softmax denominator over all E experts
 
   if (GROUPED) {
     const int gs = E / n_group;
@@ -597,17 +529,16 @@ __device__ __forceinline__ void route_wave_token(const float* __restrict__ logit
 
   // k rounds: the largest remaining key, then the lowest expert index that
   // holds it (the first item slot with a match and, inside it, the lowest
-  // lane).  Selected keys are zeroed.  Only the k winners' probabilities are
-  // ever needed, so the division by the softmax denominator happens once,
-  // after the rounds, on lanes 0..k-1.
+  // lane).  Selected keys are zeroed.  Lane j keeps winner j.
   int my_e = 0;
-  float my_z = 0.f;
-  float zsum = 0.f, zcomp = 0.f;  // compensated sum of the selected numerators
+  uint32_t my_key = 0u;
+  uint32_t top = 0u;  // the first winner's key: the largest logit (its group is kept)
   for (int j = 0; j < k; ++j) {
     uint32_t best = 0u;
 #pragma unroll
     for (int i = 0; i < IPL; ++i) best = max(best, key[i]);
     best = wave_max_u32(best);
+    top = max(top, best);  // winners come in descending order: the first one
     int item = 0;
     uint64_t hit = 0;
 #pragma unroll
@@ -619,28 +550,31 @@ __device__ __forceinline__ void route_wave_token(const float* __restrict__ logit
       }
     }
     const int owner = __builtin_ctzll(hit);
-    float cand = zv[0];
-#pragma unroll
-    for (int i = 1; i < IPL; ++i) cand = (i == item) ? zv[i] : cand;
-    const float zj = __uint_as_float(readlane(__float_as_uint(cand), owner));
 #pragma unroll
     for (int i = 0; i < IPL; ++i)
       if (i == item && lane == owner) key[i] = 0u;
     if (lane == j) {
       my_e = item * kWave + owner;
-      my_z = zj;
+      my_key = best;
     }
-    // Fast2Sum: winners come in descending order, so zsum >= zj >= 0 and the
-    // rounding error of zsum + zj is exactly zj - (ns - zsum).
+  }
+  // Winner j's numerator against the largest logit, on lane j; their total
+  // in winner order.  Fast2Sum: the winners come in descending order, so
+  // zsum >= zj >= 0 and the rounding error of zsum + zj is exactly
+  // zj - (ns - zsum).  Winner j's share of the total is its softmax
+  // probability renormalised over the k winners: the softmax denominator
+  // cancels, so it is never formed.
+  const float my_z = lane < k ? shifted_exp(key_value(my_key), key_value(top)) : 0.f;
+  float zsum = 0.f, zcomp = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const float zj = __uint_as_float(readlane(__float_as_uint(my_z), j));
     const float ns = zsum + zj;
     zcomp += zj - (ns - zsum);
     zsum = ns;
   }
   if (lane < k) {
-    const float p = my_z / s;                   // softmax probability of winner j
-    const float psel = (zsum + zcomp) / s;      // their total probability
     topk_idx[t * k + lane] = my_e;
-    topk_w[t * k + lane] = p / psel;            // renormalised to sum to 1
+    topk_w[t * k + lane] = my_z / (zsum + zcomp);
     if constexpr (COUNT) {
       const uint32_t pr = uint32_t(t * k + lane);
       __hip_atomic_fetch_add(hist_mat + size_t(pr / chunk) * E + my_e, 1, __ATOMIC_RELAXED,

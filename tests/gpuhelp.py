@@ -5,11 +5,13 @@ import torch
 
 DEV = torch.device("cuda:0")
 
-# Routing weights: the kernel's fp32 softmax + renormalisation against the
-# float64 oracle.  Rounding budget (units of u = 2^-24): exp <= 2u, softmax
-# division u, selected-sum (compensated) ~2u, final division u; with the
-# probability's own error counted twice (numerator and sum) this stays below
-# 12u, so 16u = 2^-20 relative, plus an absolute floor for fp32 underflow.
+# Routing weights: the kernel's fp32 weights against the float64 oracle's
+# renormalised softmax.  The kernel forms only the k winners' numerators
+# exp(l - l_max) (the E-term denominator cancels) and divides each by their
+# compensated sum.  Rounding budget (units of u = 2^-24): numerator <= 3u
+# (expf 2u, the fma that carries the exact difference u), counted twice
+# (numerator and sum), sum ~u, division u: below 8u, so 16u = 2^-20
+# relative, plus an absolute floor for fp32 underflow.
 W_REL = 2.0**-20
 W_ABS = 2.0**-126
 
