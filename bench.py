@@ -292,6 +292,31 @@ def main() -> int:
                "speedup_vs_bf16_recv": None}
         del buf_q, buf_s
 
+    # Group-limited routing (DeepSeek-V3's grouping: 8 groups of E/8 experts,
+    # the 4 best kept) on the same logits, timed on its own like fp8 above.
+    route_grouped = None
+    n_group, topk_group = 8, 4
+    if E % n_group == 0 and k <= topk_group * (E // n_group):
+        m.moe_route_topk_grouped(logits, k, n_group, topk_group, topk_idx=idx, topk_w=w,
+                                 stream=stream)
+        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a_, b_ in gev:
+            a_.record(stream)
+            m.moe_route_topk_grouped(logits, k, n_group, topk_group, topk_idx=idx, topk_w=w,
+                                     stream=stream)
+            b_.record(stream)
+        torch.cuda.synchronize()
+        us = 1000.0 * float(np.mean([a_.elapsed_time(b_) for a_, b_ in gev]))
+        gb = algorithmic_bytes(cfg)["route"]
+        route_grouped = {"n_group": n_group, "topk_group": topk_group, "us_mean": round(us, 2),
+                         "bytes": gb, "GBps": round(gb / (us * 1e-6) / 1e9, 1),
+                         "frac_of_peak": round(gb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+        # the headline's routing outputs again, for anything timed after this
+        m.moe_route_topk(logits, k, topk_idx=idx, topk_w=w, stream=stream)
+        torch.cuda.synchronize()
+
     # Overlap: dispatch (send + recv) on the launch stream while a stand-in
     # shared-expert GEMM, x[T,H] @ W[H, 2048] in bf16, runs on a second
     # stream (both at the default priority).  hidden = (t_dispatch + t_gemm
@@ -416,6 +441,7 @@ def main() -> int:
         "kernels": kernels,
         "kernels_cold": kernels_cold or None,
         "fp8_dispatch_recv": fp8,
+        "route_grouped": route_grouped,
         "overlap": overlap,
         "graph_replay": None if graph_ms is None else {
             "ms_per_step": round(graph_ms, 4),

@@ -18,14 +18,16 @@
 //                        cache heads of the token's lanes.  The weights are
 //                        the winners' softmax probabilities renormalised
 //                        over the k winners, formed from their k numerators
-//                        alone (the E-term denominator cancels).  Inside
-//                        moe_route_dispatch (E >= 128) the routing kernels
-//                        also count each pair into the send histogram with
-//                        an atomic add, in place of send_hist_kernel.
-//   route_wave_kernel    one wave per token (group-limited routing, and plain
-//                        routing of small batches): k rounds of a wave-wide
-//                        maximum of the keys, the lowest expert index holding
-//                        it found by ballot.
+//                        alone (the E-term denominator cancels).  It also
+//                        runs group-limited routing where every group is
+//                        1-16 whole lanes.  Inside moe_route_dispatch
+//                        (E >= 128) the routing kernels also count each pair
+//                        into the send histogram with an atomic add, in
+//                        place of send_hist_kernel.
+//   route_wave_kernel    one wave per token (small batches, and group-limited
+//                        routing the lane-group kernel cannot hold): k rounds
+//                        of a wave-wide maximum of the keys, the lowest
+//                        expert index holding it found by ballot.
 //   send_hist_kernel     per-block expert histogram; each wave groups equal
 //                        experts with ballots so the hot expert costs one LDS
 //                        update per wave, not 64.
@@ -313,6 +315,15 @@ __device__ __forceinline__ void group_sum_compensated(float& s, float& c) {
 #undef MOE_STEP
 }
 
+// The G bits of wave mask m that belong to token slot q (lanes q*G ..).
+template <int G>
+__device__ __forceinline__ uint64_t token_bits(uint64_t m, int q) {
+  if constexpr (G == kWave)
+    return m;
+  else
+    return (m >> (q * G)) & ((uint64_t(1) << G) - 1);
+}
+
 // Insert (kv, i) into a lane's cache of its C best candidates, kept in the
 // selection order: larger key first, and among equal keys the lower item
 // (= lower expert).  Items are pushed in ascending order with strict
@@ -344,10 +355,16 @@ __device__ __forceinline__ void cache_push(uint32_t kv, int i, uint32_t (&h)[C],
 // COUNT: the owner of winner j also adds the pair p = t*k + j to the send
 // histogram matrix, row p / chunk (chunk >= 64 > j, so a token's pairs span at
 // most two rows); the matrix must hold zeros beforehand.
+// GROUPED: group-limited routing (as in route_wave_kernel) where every group
+// is 2^lg whole lanes (E / n_group == 2^lg * IPL, lg <= 4): a group's score
+// is its lanes' largest key, folded over those lanes by DPP; topk_group
+// rounds of a group maximum keep the best groups (ties to the lower group),
+// and the lanes of the other groups drop their keys before the k rounds.
 // The calling wave routes tokens t_wave .. t_wave + 64/G - 1 (t_wave < T).
-template <int G, int IPL, bool VEC, bool COUNT>
+template <int G, int IPL, bool VEC, bool COUNT, bool GROUPED>
 __device__ __forceinline__ void route_topk_tile(const float* __restrict__ logits, int64_t T,
-                                                int E, int k, int32_t* __restrict__ topk_idx,
+                                                int E, int k, int topk_group, int lg,
+                                                int32_t* __restrict__ topk_idx,
                                                 float* __restrict__ topk_w,
                                                 int32_t* __restrict__ hist_mat, uint32_t chunk,
                                                 int64_t t_wave) {
@@ -389,6 +406,34 @@ __device__ __forceinline__ void route_topk_tile(const float* __restrict__ logits
 #pragma unroll
   for (int i = 0; i < IPL; ++i) key[i] = e0 + i < E ? order_key(lv[i]) : 0u;
 
+  if constexpr (GROUPED) {
+    // Every lane of group g >> lg ends up with the group's score; lanes past
+    // E form groups of their own with score 0, which no round picks (a real
+    // group's score is a nonzero key, and topk_group <= n_group).
+    uint32_t score = 0u;
+#pragma unroll
+    for (int i = 0; i < IPL; ++i) score = max(score, key[i]);
+    if (lg >= 1) score = max(score, dpp<kDppQuad1032, 0xF>(0u, score));
+    if (lg >= 2) score = max(score, dpp<kDppQuad2301, 0xF>(0u, score));
+    if (lg >= 3) score = max(score, dpp<kDppRowHalfMirror, 0xF>(0u, score));
+    if (lg >= 4) score = max(score, dpp<kDppRowMirror, 0xF>(0u, score));
+    const int my_group = g >> lg;
+    bool kept = false;
+    for (int r = 0; r < topk_group; ++r) {
+      const uint32_t best = group_max_u32<G>(score);
+      // the lowest lane with the best score lies in the lowest such group
+      const int pick = int(__builtin_ctzll(token_bits<G>(ballot(score == best), q))) >> lg;
+      if (my_group == pick) {
+        kept = true;
+        score = 0u;
+      }
+    }
+    if (!kept) {
+#pragma unroll
+      for (int i = 0; i < IPL; ++i) key[i] = 0u;
+    }
+  }
+
   uint32_t h[C];
   int hi[C];
 #pragma unroll
@@ -410,8 +455,7 @@ __device__ __forceinline__ void route_topk_tile(const float* __restrict__ logits
     bool owner = hit;
     if (__popcll(hits) > TPW) {
       // Some token has equal heads in several lanes: its lowest lane wins.
-      const uint64_t grp = G == kWave ? hits : (hits >> (q * G)) & ((uint64_t(1) << G) - 1);
-      owner = hit && (grp & ((uint64_t(1) << g) - 1)) == 0;
+      owner = hit && (token_bits<G>(hits, q) & ((uint64_t(1) << g) - 1)) == 0;
     }
     if (g == j) my_key = best;
     const uint32_t kp = h[0];
@@ -465,16 +509,17 @@ __device__ __forceinline__ void route_topk_tile(const float* __restrict__ logits
 // Waves take tiles of 64/G tokens in grid-stride order, so the grid stays
 // within the launch's 32-bit work-item count at any T.  No block barrier
 // follows the loop: a wave past T just leaves.
-template <int G, int IPL, bool VEC, bool COUNT>
+template <int G, int IPL, bool VEC, bool COUNT, bool GROUPED>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
-    const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, int32_t* __restrict__ hist_mat, uint32_t chunk) {
+    const float* __restrict__ logits, int64_t T, int E, int k, int topk_group, int lg,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ hist_mat,
+    uint32_t chunk) {
   constexpr int TPW = kWave / G;  // tokens per wave
   const int64_t stride = int64_t(gridDim.x) * kRouteWavesPerBlock * TPW;
   for (int64_t t_wave = (int64_t(blockIdx.x) * kRouteWavesPerBlock + threadIdx.x / kWave) * TPW;
        t_wave < T; t_wave += stride)
-    route_topk_tile<G, IPL, VEC, COUNT>(logits, T, E, k, topk_idx, topk_w, hist_mat, chunk,
-                                        t_wave);
+    route_topk_tile<G, IPL, VEC, COUNT, GROUPED>(logits, T, E, k, topk_group, lg, topk_idx,
+                                                 topk_w, hist_mat, chunk, t_wave);
 }
 
 // One wave per token; IPL logits per lane (expert e = lane + 64 * i).  The
@@ -1341,22 +1386,51 @@ struct RoutePlan {
   int IPL;
 };
 
-RoutePlan plan_route(int64_t T, int E, int k) {
-  RoutePlan p{};
+int route_gmin(int E, int k) {
   int gmin = E <= 384 ? 16 : (E <= 768 ? 32 : 64);
   if (k > 16 && gmin < 32) gmin = 32;
-  p.G = gmin;
+  return gmin;
+}
+
+int route_ipl(int E, int G) {  // the smallest instantiated items per lane that cover E
+  const int need = (E + G - 1) / G;
+  const int sizes[] = {1, 2, 4, 8, 16, 24};
+  for (int v : sizes)
+    if (v >= need) return v;
+  return 24;
+}
+
+RoutePlan plan_route(int64_t T, int E, int k) {
+  RoutePlan p{};
+  p.G = route_gmin(E, k);
   if (E > 128)
     while (p.G < kWave && T * p.G / kWave < 4096) p.G *= 2;
-  const int need = (E + p.G - 1) / p.G;
-  const int sizes[] = {1, 2, 4, 8, 16, 24};
-  p.IPL = 24;
-  for (int v : sizes)
-    if (v >= need) {
-      p.IPL = v;
-      break;
-    }
+  p.IPL = route_ipl(E, p.G);
   return p;
+}
+
+// Group-limited routing in the lane-group kernel needs every group to be
+// 2^lg whole lanes (lg <= 4) and 16-byte logit loads.  Of the lanes per
+// token allowed for (E, k), the plain plan's choice is tried first, then the
+// others, nearest first.  False: no plan fits; the wave kernel routes.
+bool plan_route_grouped(int64_t T, int E, int k, int n_group, const float* logits, RoutePlan& p,
+                        int& lg) {
+  if (E % 4 != 0 || !aligned(logits, 16)) return false;
+  const int gs = E / n_group;
+  const RoutePlan base = plan_route(T, E, k);
+  const int tries[3] = {base.G, base.G == 32 ? 16 : 32, base.G == 64 ? 16 : 64};
+  for (int G : tries) {
+    if (G < route_gmin(E, k)) continue;
+    const int ipl = route_ipl(E, G);
+    if (ipl % 4 != 0 || ipl * G < E || gs % ipl != 0) continue;
+    const int lanes = gs / ipl;
+    if (lanes > 16 || (lanes & (lanes - 1)) != 0) continue;
+    p.G = G;
+    p.IPL = ipl;
+    lg = __builtin_ctz(unsigned(lanes));
+    return true;
+  }
+  return false;
 }
 
 // hist_mat: nullptr, or the zero-initialised [blocks][E] send histogram
@@ -1368,6 +1442,32 @@ int enqueue_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t 
   const bool grouped = topk_group < n_group;  // keeping every group is plain top-k
   const bool count = hist_mat != nullptr;
   const uint32_t ch = uint32_t(chunk);
+  RoutePlan gp{};
+  int lg = 0;
+  if (grouped && T > kRouteWaveMaxTokens &&
+      plan_route_grouped(T, E, k, n_group, logits, gp, lg)) {
+    const int64_t tokens_per_block = int64_t(kRouteWavesPerBlock) * (kWave / gp.G);
+    const int64_t nb = (T + tokens_per_block - 1) / tokens_per_block;
+    const dim3 grid(unsigned(nb < kRouteMaxBlocks ? nb : kRouteMaxBlocks));
+#define MOE_GROUTE(G_, IPL_)                                                                    \
+  if (gp.G == G_ && gp.IPL == IPL_)                                                             \
+    return count ? launch(route_topk_kernel<G_, IPL_, true, true, true>, grid, block, 0, s,     \
+                          logits, T, E, k, topk_group, lg, topk_idx, topk_w, hist_mat, ch)      \
+                 : launch(route_topk_kernel<G_, IPL_, true, false, true>, grid, block, 0, s,    \
+                          logits, T, E, k, topk_group, lg, topk_idx, topk_w, hist_mat, ch);
+    MOE_GROUTE(16, 4);
+    MOE_GROUTE(16, 8);
+    MOE_GROUTE(16, 16);
+    MOE_GROUTE(16, 24);
+    MOE_GROUTE(32, 4);
+    MOE_GROUTE(32, 8);
+    MOE_GROUTE(32, 16);
+    MOE_GROUTE(32, 24);
+    MOE_GROUTE(64, 4);
+    MOE_GROUTE(64, 8);
+    MOE_GROUTE(64, 16);
+#undef MOE_GROUTE
+  }
   if (grouped || T <= kRouteWaveMaxTokens) {
     const int64_t nb = (T + kRouteWavesPerBlock - 1) / kRouteWavesPerBlock;
     const dim3 grid(unsigned(nb < kRouteMaxBlocks ? nb : kRouteMaxBlocks));
@@ -1396,11 +1496,11 @@ int enqueue_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t 
   const int64_t nb = (T + tokens_per_block - 1) / tokens_per_block;
   const dim3 grid(unsigned(nb < kRouteMaxBlocks ? nb : kRouteMaxBlocks));
   const bool vec = p.IPL % 4 == 0 && E % 4 == 0 && aligned(logits, 16);
-#define MOE_ROUTE_VC(G_, IPL_, VEC_)                                                            \
-  return count ? launch(route_topk_kernel<G_, IPL_, VEC_, true>, grid, block, 0, s, logits, T, \
-                        E, k, topk_idx, topk_w, hist_mat, ch)                                 \
-               : launch(route_topk_kernel<G_, IPL_, VEC_, false>, grid, block, 0, s, logits, T, \
-                        E, k, topk_idx, topk_w, hist_mat, ch)
+#define MOE_ROUTE_VC(G_, IPL_, VEC_)                                                          \
+  return count ? launch(route_topk_kernel<G_, IPL_, VEC_, true, false>, grid, block, 0, s,     \
+                        logits, T, E, k, 1, 0, topk_idx, topk_w, hist_mat, ch)                \
+               : launch(route_topk_kernel<G_, IPL_, VEC_, false, false>, grid, block, 0, s,    \
+                        logits, T, E, k, 1, 0, topk_idx, topk_w, hist_mat, ch)
 #define MOE_ROUTE(G_, IPL_)                      \
   if (p.G == G_ && p.IPL == IPL_) {              \
     if (vec) MOE_ROUTE_VC(G_, IPL_, (IPL_ % 4 == 0)); \
