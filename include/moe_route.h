@@ -83,9 +83,14 @@ const char* moe_strerror(int status);
  *            (+0.0 and -0.0 are equal).  Selecting on the logits equals
  *            selecting on the softmax probabilities, which are strictly
  *            increasing in the logits.
- *   topk_w   [T, k] fp32 (out): fp32 softmax over all E logits, then the k
- *            selected probabilities divided by their sum (sum to 1 up to fp32
- *            rounding); topk_w[t, j] belongs to topk_idx[t, j].
+ *   topk_w   [T, k] fp32 (out): the softmax probabilities of the k
+ *            selected experts divided by their sum (sum to 1 up to fp32
+ *            rounding); topk_w[t, j] belongs to topk_idx[t, j].  The E-term
+ *            softmax denominator cancels in that quotient, so it is computed
+ *            as exp(l_j - l_max) over the sum of the k such terms, within
+ *            2^-20 relative of the exact value.
+ *   Logits may be any finite values; the difference of two is not needed
+ *   to fit in fp32.
  * Errors: MOE_ERR_INVALID_ARG for T < 0, E or k out of range, null pointers.
  */
 int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,
@@ -101,8 +106,8 @@ int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,
  *   - a group's score is its largest logit;
  *   - the topk_group best groups are kept (equal scores: the lower group);
  *   - top-k, ties and weights are as in moe_route_topk, over the kept
- *     experts only; the weights are still the full-E softmax renormalised
- *     over the k chosen.
+ *     experts only; the weights are the full-E softmax probabilities
+ *     renormalised over the k chosen, as there.
  * topk_group == n_group is exactly moe_route_topk.
  * Errors: MOE_ERR_INVALID_ARG as moe_route_topk, and for n_group < 1,
  *         n_group > 64, E % n_group != 0, topk_group outside [1, n_group],
