@@ -53,10 +53,25 @@ static uint16_t bf16_of(float f) { /* round to nearest even */
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-#define HIPCHECK(x) CHECK((x) == hipSuccess)
+/* A failed HIP call ends the GPU checks: later steps would pass unset
+ * device pointers to the library. */
+#define HIPCHECK(x)                                                   \
+  do {                                                                \
+    if ((x) != hipSuccess) {                                          \
+      fprintf(stderr, "FAIL %s:%d: %s\n", __FILE__, __LINE__, #x);   \
+      ++failures;                                                     \
+      return;                                                         \
+    }                                                                 \
+  } while (0)
 
 static void gpu_checks(void) {
   enum { T = 300, E = 16, K = 4, H = 256, R = 4 };
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+    fprintf(stderr, "FAIL %s:%d: no GPU visible\n", __FILE__, __LINE__);
+    ++failures;
+    return;
+  }
   const int P = T * K;
   float* logits = malloc(sizeof(float) * T * E);
   uint16_t* x = malloc(2 * T * H);
