@@ -146,6 +146,43 @@ def test_route_logits_further_apart_than_the_fp32_range():
     assert w[1, 0] == 1.0 and np.all(w[1, 1:] == 0.0)
 
 
+@pytest.mark.parametrize("T,E,k,G,TG", [(3000, 256, 8, 8, 4), (2500, 384, 8, 8, 4),
+                                        (100, 256, 8, 8, 4)])
+def test_route_logits_only_4_byte_aligned(T, E, k, G, TG):
+    """Logits one float into their buffer: the lane-group kernel loads them
+    one float at a time, and group-limited routing falls back to the wave
+    kernel.  Plain routing equals the aligned call bit for bit; every result
+    matches the oracle; the one-call path (which counts the send histogram
+    in the routing kernel here) matches too."""
+    m = _m()
+    rng = np.random.default_rng(T + E)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    flat = torch.empty(T * E + 1, dtype=torch.float32, device=DEV)
+    mis = flat[1:].view(T, E)
+    mis.copy_(torch.from_numpy(lg))
+    assert mis.data_ptr() % 16 == 4
+    al = dev_f32(lg)
+    print(f"[edges] 4-byte aligned logits T={T} E={E} k={k} groups {TG}/{G}", flush=True)
+    a_idx, a_w = m.moe_route_topk(mis, k)
+    b_idx, b_w = m.moe_route_topk(al, k)
+    g_idx, g_w = m.moe_route_topk_grouped(mis, k, G, TG)
+    torch.cuda.synchronize()
+    assert torch.equal(a_idx, b_idx) and torch.equal(a_w.view(torch.int32), b_w.view(torch.int32))
+    r_idx, r_w, _ = oracle.route_topk(lg, k)
+    assert np.array_equal(host(a_idx), r_idx)
+    assert_weights_close(host(a_w), r_w)
+    r_idx, r_w, _ = oracle.route_topk_grouped(lg, k, G, TG)
+    assert np.array_equal(host(g_idx), r_idx)
+    assert_weights_close(host(g_w), r_w)
+    x = dev_bf16(workloads.bf16_from_f32(rng.standard_normal((T, 64)).astype(np.float32)))
+    idx, w, send, buf = m.moe_route_dispatch(mis, x, k, 8)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, b_idx) and torch.equal(w.view(torch.int32), b_w.view(torch.int32))
+    pr, rt = oracle.dispatch_slots(host(b_idx), E)
+    assert np.array_equal(host(send.pair_row), pr)
+    assert np.array_equal(host(send.row_token), rt)
+
+
 # ------------------------------------------------------------------ dispatch send
 
 def _send_check(idx, E, R):
