@@ -145,29 +145,30 @@ def test_route_dispatch_single_block_send_above_one_wave_routing(T, E, k, R):
         assert int(ws.count_nonzero().item()) == 0
 
 
-@pytest.mark.parametrize("T", [200, 300, 4096])
-def test_route_dispatch_graph_replays(T):
+@pytest.mark.parametrize("T,G,TG", [(200, 1, 1), (300, 1, 1), (4096, 1, 1), (4096, 8, 4)])
+def test_route_dispatch_graph_replays(T, G, TG):
     """The call captured once into a HIP graph and replayed three times, with
     eager work and a synchronisation between replays: every replay equals
     the eager result and leaves the workspace zero (200 tokens: routing, then
     send + recv in one launch; 300: route and send in one launch; 4096: the
-    counting route and the rank kernel that clears the matrix)."""
+    counting route and the rank kernel that clears the matrix, with plain and
+    with group-limited routing)."""
     m = _m()
     E, k, R, H = 256, 8, 32, 128
     lg, xb = _inputs(T, E, H, 5)
     logits, x = dev_f32(lg), dev_bf16(xb)
     bufs = m.MoeBuffers(T, H, E, k, R)
-    eager = [t.clone() for t in (bufs.route_dispatch(logits, x)[0], bufs.buf[: T * k])]
+    eager = [t.clone() for t in (bufs.route_dispatch(logits, x, G, TG)[0], bufs.buf[: T * k])]
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        bufs.route_dispatch(logits, x)
+        bufs.route_dispatch(logits, x, G, TG)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        bufs.route_dispatch(logits, x)
+        bufs.route_dispatch(logits, x, G, TG)
     for _ in range(3):
         bufs.topk_idx.fill_(-1)
         bufs.buf.zero_()
