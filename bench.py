@@ -29,6 +29,10 @@ SRC = os.path.join(ROOT, "combine_topk_route_amd", "csrc", "moe_route.hip")
 TRAFFIC_WORKLOAD = "dsv3_prefill"   # the workload the committed counter runs measured
 GRAPH_STEPS = 10                    # steps captured into one graph for graph_replay_multi
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", f"traffic_{TRAFFIC_WORKLOAD}.txt")
+VALU_FILE = os.path.join(ROOT, "profiles", f"valu_{TRAFFIC_WORKLOAD}.txt")
+# VALU issue peak: 256 CUs x 4 SIMDs x 2.4 GHz, a wave64 instruction taking 4
+# cycles on a 16-lane SIMD (packed fp32 is off): wave-instructions per second.
+VALU_PEAK = 256 * 4 * 2.4e9 / 4
 
 
 def algorithmic_bytes(cfg) -> dict:
@@ -54,20 +58,37 @@ def source_hash() -> str:
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
-    when there are none for this workload or the kernel source changed since
-    they were taken."""
+def _committed_count(path: str, kernel: str, workload: str):
+    """A per-launch figure from a committed rocprofv3 counter summary, or None
+    when there is none for this workload or the kernel source changed since
+    the counters were taken."""
     if workload != TRAFFIC_WORKLOAD:
         return None
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.loads(f.read().split("JSON:", 1)[1].strip().splitlines()[0])
     except (OSError, IndexError, ValueError):
         return None
     if rec.get("source_sha256_16") != source_hash():
         return None
     return rec.get("kernels", {}).get(kernel)
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE runs."""
+    return _committed_count(TRAFFIC_FILE, kernel, workload)
+
+
+def alu_roofline(kernel: str, us: float, workload: str):
+    """Routing is bound by VALU issue: its committed SQ_INSTS_VALU count per
+    launch, the time that takes at the issue peak, and that time as a share
+    of the measured launch time (None without a current count)."""
+    n = _committed_count(VALU_FILE, kernel, workload)
+    if n is None:
+        return None
+    issue_us = n / VALU_PEAK * 1e6
+    return {"bound": "alu", "valu_insts": n, "peak_winst_per_s": VALU_PEAK,
+            "issue_us": round(issue_us, 2), "frac": round(issue_us / us, 4)}
 
 
 def cpu_baseline(cfg_name: str, sample_tokens: int, seed: int) -> dict:
@@ -312,7 +333,8 @@ def main() -> int:
         gb = algorithmic_bytes(cfg)["route"]
         route_grouped = {"n_group": n_group, "topk_group": topk_group, "us_mean": round(us, 2),
                          "bytes": gb, "GBps": round(gb / (us * 1e-6) / 1e9, 1),
-                         "frac_of_peak": round(gb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+                         "frac_of_peak": round(gb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "alu": alu_roofline("route_grouped", us, cfg.name)}
         # the headline's routing outputs again, for anything timed after this
         m.moe_route_topk(logits, k, topk_idx=idx, topk_w=w, stream=stream)
         torch.cuda.synchronize()
@@ -378,6 +400,7 @@ def main() -> int:
                       "us_p90": round(1000 * float(np.percentile(per[n], 90)), 2),
                       "bytes": nbytes[n], "GBps": round(gbps, 1),
                       "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    kernels["route"]["alu"] = alu_roofline("route", kernels["route"]["us_mean"], cfg.name)
     nbytes_cold = dict(nbytes, dispatch=nbytes["dispatch_send"] + nbytes["dispatch_recv"])
     kernels_cold = {}
     for n in cold_names:

@@ -1,5 +1,6 @@
 """bench.py's host-side pieces (no GPU): the algorithmic byte counts the
-roofline uses, the counter-traffic lookup, and the one-GPU guard."""
+roofline uses, the counter-traffic and VALU-count lookups, and the one-GPU
+guard."""
 import os
 import subprocess
 import sys
@@ -26,6 +27,19 @@ def test_traffic_is_only_reported_for_the_measured_workload_and_source():
     if got is not None:  # the committed counters match the current kernel source
         alg = bench.algorithmic_bytes(workloads.CONFIGS[bench.TRAFFIC_WORKLOAD])["combine"]
         assert 1.0 <= got / alg < 1.05
+
+
+def test_alu_roofline_uses_the_committed_valu_count():
+    assert bench.alu_roofline("route", 10.0, "kimi_k2") is None
+    got = bench.alu_roofline("route", 10.0, bench.TRAFFIC_WORKLOAD)
+    if got is not None:  # the committed counters match the current kernel source
+        # 256 CUs x 4 SIMDs x 2.4 GHz / 4 cycles per wave64 instruction
+        assert got["peak_winst_per_s"] == 614.4e9
+        assert abs(got["issue_us"] - got["valu_insts"] / 614.4e3) < 0.01
+        assert abs(got["frac"] - got["valu_insts"] / 614.4e3 / 10.0) < 1e-4
+        cfg = workloads.CONFIGS[bench.TRAFFIC_WORKLOAD]
+        # the routing kernel issues a few hundred VALU instructions per token
+        assert 100 < got["valu_insts"] / cfg.T < 2000
 
 
 def test_more_than_one_gpu_is_refused():
