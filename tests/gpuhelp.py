@@ -67,3 +67,36 @@ def assert_out_close(gpu_bits, ref_bits, extra_abs=None):
     bad = ~(np.abs(g - r) <= tol)
     assert not bad.any(), f"{bad.sum()} of {bad.size} combine elements out of tolerance"
     return int(np.count_nonzero(np.asarray(gpu_bits) != np.asarray(ref_bits)))
+
+
+def assert_step_matches_oracle(logits, x_bits, k, E, R, idx, w, send, buf, y_bits=None,
+                               out=None, n_group=None, topk_group=None):
+    """One route -> dispatch (-> combine) step against the oracle: indices,
+    counts, offsets, rank offsets, pair_row, row_token and the dispatched rows
+    bit-exact; weights within 2^-20; and, given y and out, combine
+    bit-identical to the oracle's on the kernel's own fp32 weights.  ``send``
+    holds (expert_counts, expert_offsets, pair_row, row_token, rank_offsets)
+    device tensors; ``buf`` needs at least T*k rows."""
+    import oracle
+
+    T = logits.shape[0]
+    if n_group is None:
+        r_idx, r_w, _ = oracle.route_topk(logits, k)
+    else:
+        r_idx, r_w, _ = oracle.route_topk_grouped(logits, k, n_group, topk_group)
+    assert np.array_equal(host(idx)[:T], r_idx), "indices differ from the oracle"
+    assert_weights_close(host(w)[:T], r_w)
+    counts = oracle.expert_counts(r_idx, E)
+    off = oracle.expert_offsets(counts)
+    pr, rt = oracle.dispatch_slots(r_idx, E)
+    counts_g, off_g, pr_g, rt_g, rank_g = send
+    assert np.array_equal(host(counts_g), counts), "expert_counts differ"
+    assert np.array_equal(host(off_g), off), "expert_offsets differ"
+    assert np.array_equal(host(rank_g), oracle.rank_offsets(off, R)), "rank_offsets differ"
+    assert np.array_equal(host(pr_g).reshape(-1, k)[:T], pr), "pair_row differs"
+    assert np.array_equal(host(rt_g)[: T * k], rt), "row_token differs"
+    assert np.array_equal(host_bf16(buf)[: T * k], oracle.dispatch_rows(x_bits, pr, T * k)), \
+        "dispatched rows differ"
+    if out is not None:
+        ref = oracle.combine(y_bits, pr, host(w)[:T].astype(np.float32))
+        assert np.array_equal(host_bf16(out)[:T], ref), "combine differs from the oracle"

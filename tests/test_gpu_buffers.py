@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import workloads
-from gpuhelp import dev_bf16, dev_f32, host_bf16
+from gpuhelp import assert_step_matches_oracle, dev_bf16, dev_f32, host_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -60,20 +60,25 @@ def test_buffers_match_plain_calls_and_do_not_allocate():
 
 
 def test_buffers_in_a_graph_with_a_smaller_batch():
+    """A batch smaller than max_tokens captured into a HIP graph: every
+    replay, and a replay on new inputs, matches the oracle (routing,
+    dispatch and combine on the kernel's own weights) and the eager run."""
     import combine_topk_route_amd as m
 
     cfg = workloads.CONFIGS["dsv3_decode"]
     mb = m.MoeBuffers(256, cfg.H, cfg.E, cfg.k, cfg.R)
     wl = workloads.make(cfg, seed=11)
+    wl2 = workloads.make(cfg, seed=12, with_y=False)
     logits, x, y = dev_f32(wl.logits), dev_bf16(wl.x), dev_bf16(wl.y)
     print("[buffers] graph capture, T=128 of max 256", flush=True)
 
     def step():
         idx, w = mb.route(logits)
         send, buf = mb.dispatch(idx, x)
-        return mb.combine(y, send.pair_row, w)
+        return idx, w, send, buf, mb.combine(y, send.pair_row, w)
 
-    eager = host_bf16(step()).copy()
+    res = step()
+    eager = host_bf16(res[4]).copy()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -82,10 +87,19 @@ def test_buffers_in_a_graph_with_a_smaller_batch():
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        out = step()
+        step()
     for _ in range(3):
         mb.out.fill_(0)
+        mb.buf.zero_()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert np.array_equal(host_bf16(out), eager)
+        assert np.array_equal(host_bf16(res[4]), eager)
+        assert_step_matches_oracle(wl.logits, wl.x, cfg.k, cfg.E, cfg.R, *res[:4], y_bits=wl.y,
+                                   out=res[4])
+    logits.copy_(dev_f32(wl2.logits))
+    x.copy_(dev_bf16(wl2.x))
+    g.replay()
+    torch.cuda.synchronize()
+    assert_step_matches_oracle(wl2.logits, wl2.x, cfg.k, cfg.E, cfg.R, *res[:4], y_bits=wl.y,
+                               out=res[4])

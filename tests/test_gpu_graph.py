@@ -1,12 +1,14 @@
 """HIP-graph capture of the whole path: launches are sized from T*k only, so
-one captured graph serves any routing.  Every replay is checked against the
-eager result, with eager work and synchronisations between replays."""
+one captured graph serves any routing.  Every replay, with eager work and
+synchronisations between replays, is checked against the oracle (indices,
+counts, offsets, rows and dispatched bytes bit-exact, weights within 2^-20,
+combine bit-identical on the kernel's weights) and against the eager run."""
 import numpy as np
 import pytest
 import torch
 
 import workloads
-from gpuhelp import DEV, dev_bf16, dev_f32, host, host_bf16
+from gpuhelp import DEV, assert_step_matches_oracle, dev_bf16, dev_f32, host, host_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -47,6 +49,11 @@ def test_graph_replays_match_eager(name):
     def snapshot():
         return [host_bf16(t) if t.dtype == torch.bfloat16 else host(t) for t in outs]
 
+    def check_oracle(w_in):
+        assert_step_matches_oracle(w_in.logits, w_in.x, k, E, R, idx, w,
+                                   (counts, offsets, pair_row, row_token, rank_off), buf,
+                                   y_bits=wl.y, out=out)
+
     main = torch.cuda.current_stream()
     step(main)
     torch.cuda.synchronize()
@@ -72,6 +79,7 @@ def test_graph_replays_match_eager(name):
         got = snapshot()
         for a, b in zip(got, eager):
             assert np.array_equal(a, b), f"replay {rep} differs from eager"
+        check_oracle(wl)
 
     # new routing inputs, same graph: the replay must equal a fresh eager run
     logits.copy_(dev_f32(wl2.logits))
@@ -79,6 +87,7 @@ def test_graph_replays_match_eager(name):
     g.replay()
     torch.cuda.synchronize()
     got = snapshot()
+    check_oracle(wl2)
     step(main)
     torch.cuda.synchronize()
     for a, b in zip(got, snapshot()):

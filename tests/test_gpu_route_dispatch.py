@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import workloads
-from gpuhelp import DEV, dev_bf16, dev_f32, host, host_bf16
+from gpuhelp import DEV, assert_step_matches_oracle, dev_bf16, dev_f32, host, host_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -148,18 +148,22 @@ def test_route_dispatch_single_block_send_above_one_wave_routing(T, E, k, R):
 @pytest.mark.parametrize("T,G,TG", [(200, 1, 1), (300, 1, 1), (4096, 1, 1), (4096, 8, 4)])
 def test_route_dispatch_graph_replays(T, G, TG):
     """The call captured once into a HIP graph and replayed three times, with
-    eager work and a synchronisation between replays: every replay equals
-    the eager result and leaves the workspace zero (200 tokens: routing, then
-    send + recv in one launch; 300: route and send in one launch; 4096: the
-    counting route and the rank kernel that clears the matrix, with plain and
-    with group-limited routing)."""
+    eager work and a synchronisation between replays, then once more on new
+    inputs: every replay matches the oracle (indices, counts, offsets, rows
+    and dispatched bytes bit-exact, weights within 2^-20) and the eager
+    result, and leaves the workspace zero (200 tokens: routing, then send +
+    recv in one launch; 300: route and send in one launch; 4096: the counting
+    route and the rank kernel that clears the matrix, with plain and with
+    group-limited routing)."""
     m = _m()
     E, k, R, H = 256, 8, 32, 128
     lg, xb = _inputs(T, E, H, 5)
     logits, x = dev_f32(lg), dev_bf16(xb)
     bufs = m.MoeBuffers(T, H, E, k, R)
-    eager = [t.clone() for t in (bufs.route_dispatch(logits, x, G, TG)[0], bufs.buf[: T * k])]
+    res = bufs.route_dispatch(logits, x, G, TG)
+    eager = [t.clone() for t in (res[0], bufs.buf[: T * k])]
     torch.cuda.synchronize()
+    groups = dict(n_group=G, topk_group=TG) if TG < G else {}
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -169,15 +173,24 @@ def test_route_dispatch_graph_replays(T, G, TG):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         bufs.route_dispatch(logits, x, G, TG)
-    for _ in range(3):
+    for rep in range(3):
         bufs.topk_idx.fill_(-1)
         bufs.buf.zero_()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
+        print(f"[route_dispatch] graph T={T} groups {TG}/{G}: replay {rep}", flush=True)
         assert torch.equal(bufs.topk_idx[:T], eager[0])
         assert torch.equal(bufs.buf[: T * k].view(torch.int16), eager[1].view(torch.int16))
+        assert_step_matches_oracle(lg, xb, k, E, R, res[0], res[1], res[2], res[3], **groups)
         assert int(bufs.route_workspace.count_nonzero().item()) == 0
+    lg2, xb2 = _inputs(T, E, H, 6)  # new inputs, same graph
+    logits.copy_(dev_f32(lg2))
+    x.copy_(dev_bf16(xb2))
+    g.replay()
+    torch.cuda.synchronize()
+    assert_step_matches_oracle(lg2, xb2, k, E, R, res[0], res[1], res[2], res[3], **groups)
+    assert int(bufs.route_workspace.count_nonzero().item()) == 0
 
 
 @pytest.mark.parametrize("T,E,k,G,TG,R", [

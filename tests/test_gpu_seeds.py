@@ -42,7 +42,8 @@ def test_whole_path_at_more_seeds(name, seed):
     assert np.array_equal(host(send.pair_row), pr)
     assert np.array_equal(host(send.row_token), rt)
     assert np.array_equal(host_bf16(buf), wl.x[rt])
-    tokens = np.arange(cfg.T) if cfg.T * cfg.H <= 4096 * 4096 else \
-        np.unique(np.random.default_rng(seed).choice(cfg.T, 256, replace=False))
-    ref = oracle.combine_tokens(wl.y, pr, r_w32, tokens)
-    assert assert_out_close(host_bf16(out)[tokens], ref) == 0
+    got = host_bf16(out)
+    for t0 in range(0, cfg.T, 1024):  # every token, the oracle in chunks
+        tokens = np.arange(t0, min(cfg.T, t0 + 1024))
+        ref = oracle.combine_tokens(wl.y, pr, r_w32, tokens)
+        assert assert_out_close(got[tokens], ref) == 0
