@@ -3,11 +3,14 @@
 Every function has the name of the C entry point it calls, checks tensor
 placement / dtype / contiguity, allocates outputs the caller did not pass
 (torch is the device-memory and stream provider), and passes raw pointers
-plus the current HIP stream.  All computation runs in the library's kernels;
-there is no other path.  A non-zero status raises ``MoeError``.
+plus the launch stream (the current one unless ``stream=`` names another;
+anything the binding allocates is allocated on that stream).  All
+computation runs in the library's kernels; there is no other path.  A
+non-zero status raises ``MoeError``.
 """
 from __future__ import annotations
 
+import contextlib
 from typing import NamedTuple, Optional
 
 import torch
@@ -45,6 +48,20 @@ def _stream(stream, like: torch.Tensor) -> int:
     return int(stream)
 
 
+def _on(stream, like: torch.Tensor):
+    """Context for the binding's own allocations (outputs the caller did not
+    pass, scratch): the launch stream.  torch's caching allocator then hands
+    a freed block out again only to later work on that stream, and the fill
+    of ``torch.zeros`` runs on it, so both are ordered with the kernels this
+    call enqueues there.  ``stream=None`` launches on the current stream,
+    which is where torch allocates anyway."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream), device=like.device)
+    return torch.cuda.stream(stream)
+
+
 def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: Optional[int] = None,
          device: Optional[int] = None) -> int:
     """Device pointer of `t` after checking placement, dtype, rank and layout.
@@ -74,8 +91,9 @@ def _reject(t, name: str, dtype: torch.dtype, ndim: Optional[int], device: Optio
     raise ValueError(f"{name} must be contiguous")
 
 
-def _empty(shape, dtype, like: torch.Tensor) -> torch.Tensor:
-    return torch.empty(shape, dtype=dtype, device=like.device)
+def _empty(shape, dtype, like: torch.Tensor, stream) -> torch.Tensor:
+    with _on(stream, like):
+        return torch.empty(shape, dtype=dtype, device=like.device)
 
 
 def moe_abi_version() -> int:
@@ -89,9 +107,9 @@ def moe_route_topk(logits: torch.Tensor, k: int, topk_idx: Optional[torch.Tensor
     d = logits.get_device()
     T, E = logits.shape
     if topk_idx is None:
-        topk_idx = _empty((T, k), torch.int32, logits)
+        topk_idx = _empty((T, k), torch.int32, logits, stream)
     if topk_w is None:
-        topk_w = _empty((T, k), torch.float32, logits)
+        topk_w = _empty((T, k), torch.float32, logits, stream)
     ip = _dev(topk_idx, "topk_idx", torch.int32, device=d)
     wp = _dev(topk_w, "topk_w", torch.float32, device=d)
     if topk_idx.numel() != T * k or topk_w.numel() != T * k:
@@ -108,9 +126,9 @@ def moe_route_topk_grouped(logits: torch.Tensor, k: int, n_group: int, topk_grou
     d = logits.get_device()
     T, E = logits.shape
     if topk_idx is None:
-        topk_idx = _empty((T, k), torch.int32, logits)
+        topk_idx = _empty((T, k), torch.int32, logits, stream)
     if topk_w is None:
-        topk_w = _empty((T, k), torch.float32, logits)
+        topk_w = _empty((T, k), torch.float32, logits, stream)
     ip = _dev(topk_idx, "topk_idx", torch.int32, device=d)
     wp = _dev(topk_w, "topk_w", torch.float32, device=d)
     if topk_idx.numel() != T * k or topk_w.numel() != T * k:
@@ -133,18 +151,18 @@ class SendResult(NamedTuple):
 
 
 def _send_outputs(topk_idx, E, R, expert_counts, expert_offsets, pair_row, row_token,
-                  rank_offsets, with_rank_offsets):
+                  rank_offsets, with_rank_offsets, stream):
     T, k = topk_idx.shape
     if expert_counts is None:
-        expert_counts = _empty((E,), torch.int32, topk_idx)
+        expert_counts = _empty((E,), torch.int32, topk_idx, stream)
     if expert_offsets is None:
-        expert_offsets = _empty((E + 1,), torch.int32, topk_idx)
+        expert_offsets = _empty((E + 1,), torch.int32, topk_idx, stream)
     if pair_row is None:
-        pair_row = _empty((T, k), torch.int32, topk_idx)
+        pair_row = _empty((T, k), torch.int32, topk_idx, stream)
     if row_token is None:
-        row_token = _empty((T * k,), torch.int32, topk_idx)
+        row_token = _empty((T * k,), torch.int32, topk_idx, stream)
     if rank_offsets is None and with_rank_offsets:
-        rank_offsets = _empty((R + 1,), torch.int32, topk_idx)
+        rank_offsets = _empty((R + 1,), torch.int32, topk_idx, stream)
     sizes = [(expert_counts, E), (expert_offsets, E + 1), (pair_row, T * k), (row_token, T * k)]
     if rank_offsets is not None:
         sizes.append((rank_offsets, R + 1))
@@ -154,14 +172,14 @@ def _send_outputs(topk_idx, E, R, expert_counts, expert_offsets, pair_row, row_t
     return SendResult(expert_counts, expert_offsets, pair_row, row_token, rank_offsets)
 
 
-def _workspace(T, E, k, workspace, like):
+def _workspace(T, E, k, workspace, like, stream):
     """(pointer, bytes, tensor) of the send workspace; allocated here when the
     caller passed none and the launch needs one.  The library checks the size."""
     if workspace is None:
         need = moe_dispatch_workspace_bytes(T, E, k)
         if need == 0:
             return 0, 0, None
-        workspace = torch.empty((need,), dtype=torch.uint8, device=like.device)
+        workspace = _empty((need,), torch.uint8, like, stream)
     return (_dev(workspace, "workspace", torch.uint8, device=like.get_device()), workspace.numel(),
             workspace)
 
@@ -185,8 +203,8 @@ def moe_dispatch_send(topk_idx: torch.Tensor, E: int, num_vranks: int = 1, *,
     d = topk_idx.get_device()
     T, k = topk_idx.shape
     out = _send_outputs(topk_idx, E, num_vranks, expert_counts, expert_offsets, pair_row,
-                        row_token, rank_offsets, with_rank_offsets)
-    wp, wn, _ = _workspace(T, E, k, workspace, topk_idx)
+                        row_token, rank_offsets, with_rank_offsets, stream)
+    wp, wn, _ = _workspace(T, E, k, workspace, topk_idx, stream)
     cp, op, pp, tp, rp = _send_ptrs(out, d)
     _check("moe_dispatch_send", _lib.load().moe_dispatch_send(
         ip, T, E, k, num_vranks, cp, op, pp, tp, rp, wp, wn, _stream(stream, topk_idx)))
@@ -202,7 +220,7 @@ def moe_dispatch_recv(x: torch.Tensor, pair_row: torch.Tensor, buf: Optional[tor
     if pair_row.dim() != 2 or pair_row.shape[0] != T:
         raise ValueError("pair_row must be [T, k]")
     if buf is None:
-        buf = _empty((T * k if capacity is None else capacity, H), torch.bfloat16, x)
+        buf = _empty((T * k if capacity is None else capacity, H), torch.bfloat16, x, stream)
     if capacity is None:
         capacity = buf.shape[0]
     if buf.dim() != 2 or buf.shape[1] != H or buf.shape[0] < capacity:
@@ -227,14 +245,14 @@ def moe_dispatch(topk_idx: torch.Tensor, x: torch.Tensor, E: int, num_vranks: in
     if x.shape[0] != T:
         raise ValueError("x and topk_idx disagree on T")
     out = _send_outputs(topk_idx, E, num_vranks, expert_counts, expert_offsets, pair_row,
-                        row_token, rank_offsets, with_rank_offsets)
+                        row_token, rank_offsets, with_rank_offsets, stream)
     if buf is None:
-        buf = _empty((T * k if capacity is None else capacity, H), torch.bfloat16, x)
+        buf = _empty((T * k if capacity is None else capacity, H), torch.bfloat16, x, stream)
     if capacity is None:
         capacity = buf.shape[0]
     if buf.dim() != 2 or buf.shape[1] != H or buf.shape[0] < capacity:
         raise ValueError("buf must be [>= capacity, H]")
-    wp, wn, _ = _workspace(T, E, k, workspace, topk_idx)
+    wp, wn, _ = _workspace(T, E, k, workspace, topk_idx, stream)
     cp, op, pp, tp, rp = _send_ptrs(out, d)
     _check("moe_dispatch", _lib.load().moe_dispatch(
         ip, xp, T, E, k, H, num_vranks, cp, op, pp, tp, rp,
@@ -265,24 +283,25 @@ def moe_route_dispatch(logits: torch.Tensor, x: torch.Tensor, k: int, num_vranks
     if x.shape[0] != T:
         raise ValueError("x and logits disagree on T")
     if topk_idx is None:
-        topk_idx = _empty((T, k), torch.int32, logits)
+        topk_idx = _empty((T, k), torch.int32, logits, stream)
     if topk_w is None:
-        topk_w = _empty((T, k), torch.float32, logits)
+        topk_w = _empty((T, k), torch.float32, logits, stream)
     if topk_idx.shape != (T, k) or topk_w.shape != (T, k):
         raise ValueError("topk_idx / topk_w must be [T, k]")
     ip = _dev(topk_idx, "topk_idx", torch.int32, device=d)
     wp = _dev(topk_w, "topk_w", torch.float32, device=d)
     out = _send_outputs(topk_idx, E, num_vranks, expert_counts, expert_offsets, pair_row,
-                        row_token, rank_offsets, with_rank_offsets)
+                        row_token, rank_offsets, with_rank_offsets, stream)
     if buf is None:
-        buf = _empty((T * k if capacity is None else capacity, H), torch.bfloat16, x)
+        buf = _empty((T * k if capacity is None else capacity, H), torch.bfloat16, x, stream)
     if capacity is None:
         capacity = buf.shape[0]
     if buf.dim() != 2 or buf.shape[1] != H or buf.shape[0] < capacity:
         raise ValueError("buf must be [>= capacity, H]")
     if workspace is None:
-        workspace = torch.zeros((max(1, moe_route_dispatch_workspace_bytes(T, E, k)),),
-                                dtype=torch.uint8, device=logits.device)
+        with _on(stream, logits):  # zero-filled on the launch stream
+            workspace = torch.zeros((max(1, moe_route_dispatch_workspace_bytes(T, E, k)),),
+                                    dtype=torch.uint8, device=logits.device)
     wsp = _dev(workspace, "workspace", torch.uint8, device=d)
     cp, op, pp, tp, rp = _send_ptrs(out, d)
     _check("moe_route_dispatch", _lib.load().moe_route_dispatch(
@@ -292,13 +311,13 @@ def moe_route_dispatch(logits: torch.Tensor, x: torch.Tensor, k: int, num_vranks
     return topk_idx, topk_w, out, buf
 
 
-def _fp8_bufs(x, T, k, buf_q, buf_scale, capacity):
+def _fp8_bufs(x, T, k, buf_q, buf_scale, capacity, stream):
     H = x.shape[1]
     rows = T * k if capacity is None else capacity
     if buf_q is None:
-        buf_q = _empty((rows, H), torch.uint8, x)
+        buf_q = _empty((rows, H), torch.uint8, x, stream)
     if buf_scale is None:
-        buf_scale = _empty((rows, H // 128 if H % 128 == 0 else 0), torch.float32, x)
+        buf_scale = _empty((rows, H // 128 if H % 128 == 0 else 0), torch.float32, x, stream)
     if capacity is None:
         capacity = buf_q.shape[0]
     if buf_q.dim() != 2 or buf_q.shape[1] != H or buf_q.shape[0] < capacity:
@@ -317,7 +336,7 @@ def moe_dispatch_recv_fp8(x: torch.Tensor, pair_row: torch.Tensor, buf_q=None, b
     if pair_row.dim() != 2 or pair_row.shape[0] != T:
         raise ValueError("pair_row must be [T, k]")
     k = pair_row.shape[1]
-    buf_q, buf_scale, capacity = _fp8_bufs(x, T, k, buf_q, buf_scale, capacity)
+    buf_q, buf_scale, capacity = _fp8_bufs(x, T, k, buf_q, buf_scale, capacity, stream)
     d = x.get_device()
     _check("moe_dispatch_recv_fp8", _lib.load().moe_dispatch_recv_fp8(
         xp, _dev(pair_row, "pair_row", torch.int32, device=d), T, H, k,
@@ -339,9 +358,9 @@ def moe_dispatch_fp8(topk_idx: torch.Tensor, x: torch.Tensor, E: int, num_vranks
     if x.shape[0] != T:
         raise ValueError("x and topk_idx disagree on T")
     out = _send_outputs(topk_idx, E, num_vranks, expert_counts, expert_offsets, pair_row,
-                        row_token, rank_offsets, with_rank_offsets)
-    buf_q, buf_scale, capacity = _fp8_bufs(x, T, k, buf_q, buf_scale, capacity)
-    wp, wn, _ = _workspace(T, E, k, workspace, topk_idx)
+                        row_token, rank_offsets, with_rank_offsets, stream)
+    buf_q, buf_scale, capacity = _fp8_bufs(x, T, k, buf_q, buf_scale, capacity, stream)
+    wp, wn, _ = _workspace(T, E, k, workspace, topk_idx, stream)
     cp, op, pp, tp, rp = _send_ptrs(out, d)
     _check("moe_dispatch_fp8", _lib.load().moe_dispatch_fp8(
         ip, xp, T, E, k, H, num_vranks, cp, op, pp, tp, rp,
@@ -368,19 +387,20 @@ def moe_route_dispatch_fp8(logits: torch.Tensor, x: torch.Tensor, k: int, num_vr
     if x.shape[0] != T:
         raise ValueError("x and logits disagree on T")
     if topk_idx is None:
-        topk_idx = _empty((T, k), torch.int32, logits)
+        topk_idx = _empty((T, k), torch.int32, logits, stream)
     if topk_w is None:
-        topk_w = _empty((T, k), torch.float32, logits)
+        topk_w = _empty((T, k), torch.float32, logits, stream)
     if topk_idx.shape != (T, k) or topk_w.shape != (T, k):
         raise ValueError("topk_idx / topk_w must be [T, k]")
     ip = _dev(topk_idx, "topk_idx", torch.int32, device=d)
     wp = _dev(topk_w, "topk_w", torch.float32, device=d)
     out = _send_outputs(topk_idx, E, num_vranks, expert_counts, expert_offsets, pair_row,
-                        row_token, rank_offsets, with_rank_offsets)
-    buf_q, buf_scale, capacity = _fp8_bufs(x, T, k, buf_q, buf_scale, capacity)
+                        row_token, rank_offsets, with_rank_offsets, stream)
+    buf_q, buf_scale, capacity = _fp8_bufs(x, T, k, buf_q, buf_scale, capacity, stream)
     if workspace is None:
-        workspace = torch.zeros((max(1, moe_route_dispatch_workspace_bytes(T, E, k)),),
-                                dtype=torch.uint8, device=logits.device)
+        with _on(stream, logits):  # zero-filled on the launch stream
+            workspace = torch.zeros((max(1, moe_route_dispatch_workspace_bytes(T, E, k)),),
+                                    dtype=torch.uint8, device=logits.device)
     wsp = _dev(workspace, "workspace", torch.uint8, device=d)
     cp, op, pp, tp, rp = _send_ptrs(out, d)
     _check("moe_route_dispatch_fp8", _lib.load().moe_route_dispatch_fp8(
@@ -407,7 +427,7 @@ def moe_combine(y: torch.Tensor, pair_row: torch.Tensor, topk_w: torch.Tensor,
     if capacity > y.shape[0]:
         raise ValueError("capacity exceeds y's rows")
     if out is None:
-        out = _empty((T, H), torch.bfloat16, y)
+        out = _empty((T, H), torch.bfloat16, y, stream)
     if out.shape != (T, H):
         raise ValueError("out must be [T, H]")
     d = y.get_device()

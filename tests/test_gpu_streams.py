@@ -97,3 +97,45 @@ def test_route_dispatch_on_two_streams_at_once(sizes):
         assert np.array_equal(host(send.pair_row), pr)
         assert np.array_equal(host_bf16(buf), xb[rt])
         assert int(ws.count_nonzero().item()) == 0
+
+
+def test_binding_allocates_on_the_launch_stream():
+    """Called with ``stream=`` a side stream and no outputs or workspace, the
+    binding allocates them (and zero-fills moe_route_dispatch's workspace) on
+    that stream.  The side stream is kept busy first, and work on the current
+    stream right after each call allocates and fills blocks of the same size;
+    the results must still match the oracle."""
+    import combine_topk_route_amd as m
+    from gpuhelp import DEV, assert_step_matches_oracle
+
+    T, E, k, R, H = 4096, 256, 8, 32, 512
+    rng = np.random.default_rng(21)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    xb = workloads.bf16_from_f32(rng.standard_normal((T, H)).astype(np.float32))
+    logits, x = dev_f32(lg), dev_bf16(xb)
+    side = torch.cuda.Stream()
+    busy = torch.ones((1 << 26,), device=DEV)
+    ws_send = m.moe_dispatch_workspace_bytes(T, E, k)
+    ws_route = m.moe_route_dispatch_workspace_bytes(T, E, k)
+    assert ws_send > 0 and ws_route > 0
+    torch.cuda.synchronize()
+    for rep in range(3):
+        print(f"[streams] binding allocations on a side stream, rep {rep}", flush=True)
+        with torch.cuda.stream(side):
+            busy.mul_(1.0)
+        idx, w = m.moe_route_topk(logits, k, stream=side)
+        send = m.moe_dispatch_send(idx, E, R, stream=side)
+        junk = [torch.full((n,), 0x5A, dtype=torch.uint8, device=DEV)
+                for n in (ws_send, ws_route, T * k * 4)]
+        buf = m.moe_dispatch_recv(x, send.pair_row, stream=side)
+        torch.cuda.synchronize()
+        assert_step_matches_oracle(lg, xb, k, E, R, idx, w, send, buf)
+        del junk
+        with torch.cuda.stream(side):
+            busy.mul_(1.0)
+        idx2, w2, send2, buf2 = m.moe_route_dispatch(logits, x, k, R, stream=side)
+        junk = [torch.full((n,), 0x5A, dtype=torch.uint8, device=DEV)
+                for n in (ws_send, ws_route, T * k * 4)]
+        torch.cuda.synchronize()
+        assert_step_matches_oracle(lg, xb, k, E, R, idx2, w2, send2, buf2)
+        del junk, idx, w, send, buf, idx2, w2, send2, buf2
