@@ -30,6 +30,15 @@ TRAFFIC_WORKLOAD = "dsv3_prefill"   # the workload the committed counter runs me
 GRAPH_STEPS = 10                    # steps captured into one graph for graph_replay_multi
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", f"traffic_{TRAFFIC_WORKLOAD}.txt")
 VALU_FILE = os.path.join(ROOT, "profiles", f"valu_{TRAFFIC_WORKLOAD}.txt")
+TRACE_FILE = os.path.join(ROOT, "profiles", f"kernels_{TRAFFIC_WORKLOAD}.md")
+# Where the timed launches find their inputs.
+CACHE_STATE = {
+    "step": ("device memory; steps back to back, so x (read once per step) stays in the "
+             "256 MiB Infinity Cache from one step to the next, while y, buf and out stream "
+             "through HBM"),
+    "warm": "steady state: launches back to back, x cache-resident from the previous step",
+    "cold": "every cache flushed before each launch (1 GiB read sweep): all inputs from HBM",
+}
 # VALU issue peak: 256 CUs x 4 SIMDs x 2.4 GHz, a wave64 instruction taking 4
 # cycles on a 16-lane SIMD (packed fp32 is off): wave-instructions per second.
 VALU_PEAK = 256 * 4 * 2.4e9 / 4
@@ -58,10 +67,10 @@ def source_hash() -> str:
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def _committed_count(path: str, kernel: str, workload: str):
-    """A per-launch figure from a committed rocprofv3 counter summary, or None
-    when there is none for this workload or the kernel source changed since
-    the counters were taken."""
+def _committed_count(path: str, kernel: str, workload: str, section: str = "kernels"):
+    """A per-launch figure from a committed rocprofv3 summary (its JSON line,
+    `section` of it), or None when there is none for this workload or the
+    kernel source changed since the profile was taken."""
     if workload != TRAFFIC_WORKLOAD:
         return None
     try:
@@ -71,12 +80,14 @@ def _committed_count(path: str, kernel: str, workload: str):
         return None
     if rec.get("source_sha256_16") != source_hash():
         return None
-    return rec.get("kernels", {}).get(kernel)
+    return rec.get(section, {}).get(kernel)
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE runs."""
-    return _committed_count(TRAFFIC_FILE, kernel, workload)
+def measured_traffic(kernel: str, workload: str, cold: bool = False):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE runs
+    (the launches after the cache flush when `cold`)."""
+    return _committed_count(TRAFFIC_FILE, kernel, workload,
+                            "kernels_cold" if cold else "kernels")
 
 
 def alu_roofline(kernel: str, us: float, workload: str):
@@ -122,6 +133,65 @@ def cpu_baseline(cfg_name: str, sample_tokens: int, seed: int) -> dict:
     }
 
 
+# Tokens of each workload the per-config oracle table times (a few seconds
+# of numpy each on one core).
+CPU_TABLE_TOKENS = {"tiny": 16, "mixtral": 2048, "dsv3_decode": 128, "dsv3_prefill": 1024,
+                    "kimi_k2": 1024}
+
+
+def cpu_table(seed: int) -> dict:
+    """The oracle timed on every workload (a bounded prefix of each, stages
+    timed separately), and Tiny also in brute-force mode: exhaustive k-subset
+    search for routing and exact rational arithmetic for every fma of
+    combine.  numpy runs these element-wise loops on one core."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    rows = []
+    for name, n in CPU_TABLE_TOKENS.items():
+        wl = workloads.make(name, seed=seed, T=n)
+        cfg = wl.cfg
+        t0 = time.perf_counter()
+        idx, _, w32 = oracle.route_topk(wl.logits, cfg.k)
+        t1 = time.perf_counter()
+        counts = oracle.expert_counts(idx, cfg.E)
+        oracle.expert_offsets(counts)
+        pr, _ = oracle.dispatch_slots(idx, cfg.E)
+        oracle.dispatch_rows(wl.x, pr, n * cfg.k)
+        t2 = time.perf_counter()
+        oracle.combine(wl.y, pr, w32)
+        t3 = time.perf_counter()
+        nb = algorithmic_bytes(dataclass_replace_T(cfg, n))
+        rows.append({"workload": name, "tokens": n, "of": cfg.T, "route_s": round(t1 - t0, 4),
+                     "dispatch_s": round(t2 - t1, 4), "combine_s": round(t3 - t2, 4),
+                     "tokens_per_s": round(n / (t3 - t0), 1),
+                     "dispatch_combine_GBps": round(
+                         (nb["dispatch_recv"] + nb["combine"]) / (t3 - t1) / 1e9, 3)})
+        if name == "tiny":
+            t0 = time.perf_counter()
+            sets = oracle.route_topk_bruteforce(wl.logits, cfg.k)
+            t1 = time.perf_counter()
+            exact = oracle.combine_exact(wl.y, pr, w32)
+            t2 = time.perf_counter()
+            assert [tuple(sorted(r)) for r in idx.tolist()] == [tuple(s_) for s_ in sets]
+            assert np.array_equal(exact, oracle.combine(wl.y, pr, w32))
+            rows.append({"workload": "tiny (brute force)", "tokens": n, "of": cfg.T,
+                         "route_s": round(t1 - t0, 4), "combine_s": round(t2 - t1, 4),
+                         "tokens_per_s": round(n / (t2 - t0), 1),
+                         "note": "exhaustive subset search; exact-rational fma chain; "
+                                 "both agree with the vectorised oracle"})
+    return {"cpu_oracle_table": rows, "cores": 1, "cpu_count": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0)), "seed": seed}
+
+
+def dataclass_replace_T(cfg, T: int):
+    import dataclasses
+
+    return dataclasses.replace(cfg, T=T)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,7 +205,13 @@ def main() -> int:
     ap.add_argument("--no-overlap", action="store_true", help="skip the two-stream overlap timing")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache timing (keeps a kernel trace to warm launches only)")
+    ap.add_argument("--cpu-table", action="store_true",
+                    help="time the CPU oracle on every workload (host only) and exit")
     args = ap.parse_args()
+
+    if args.cpu_table:
+        print(json.dumps(cpu_table(args.seed)), flush=True)
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -218,6 +294,33 @@ def main() -> int:
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
+
+    # Routing alone, back to back on the GPU: K launches captured into one
+    # HIP graph and replayed once (an event pair per launch adds a few
+    # microseconds of record overhead, the size of the kernel itself, and
+    # eager launches from Python can leave the GPU waiting for the host).
+    route_b2b_us = None
+    if not args.no_graph:
+        gr = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            m.moe_route_topk(logits, k, topk_idx=idx, topk_w=w, stream=side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gr):
+            for _ in range(args.steps):
+                m.moe_route_topk(logits, k, topk_idx=idx, topk_w=w,
+                                 stream=torch.cuda.current_stream())
+        gr.replay()
+        torch.cuda.synchronize()
+        ra, rb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ra.record(stream)
+        gr.replay()
+        rb.record(stream)
+        torch.cuda.synchronize()
+        route_b2b_us = ra.elapsed_time(rb) * 1000.0 / args.steps
+        del gr
 
     # Timed region 3: the step captured once into a HIP graph (no host-side
     # knowledge of routed counts is needed, so one graph serves any routing)
@@ -400,18 +503,45 @@ def main() -> int:
                       "us_p90": round(1000 * float(np.percentile(per[n], 90)), 2),
                       "bytes": nbytes[n], "GBps": round(gbps, 1),
                       "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
-    kernels["route"]["alu"] = alu_roofline("route", kernels["route"]["us_mean"], cfg.name)
+    if route_b2b_us is not None:
+        kernels["route"]["us_back_to_back"] = round(route_b2b_us, 2)
+    kernels["route"]["alu"] = alu_roofline(
+        "route", route_b2b_us if route_b2b_us is not None else kernels["route"]["us_mean"],
+        cfg.name)
+    # The counting routing kernel of the headline step runs inside
+    # moe_route_dispatch, where no event can bracket it: its time is the
+    # committed kernel trace's average for the same code.
+    trace_us = _committed_count(TRACE_FILE, "route_counting", cfg.name)
+    if trace_us is not None:
+        a_ = alu_roofline("route_counting", trace_us, cfg.name)
+        if a_ is not None:
+            kernels["route"]["alu_counting"] = dict(a_, us_trace=trace_us)
     nbytes_cold = dict(nbytes, dispatch=nbytes["dispatch_send"] + nbytes["dispatch_recv"])
     kernels_cold = {}
     for n in cold_names:
         d = [a_.elapsed_time(b_) for a_, b_ in cold_ev[n]]
         med = 1000.0 * float(np.median(d))
-        kernels_cold[n] = {"us_median": round(med, 2),
+        mean = 1000.0 * float(np.mean(d))
+        kernels_cold[n] = {"us_mean": round(mean, 2), "us_median": round(med, 2),
                            "us_p10": round(1000 * float(np.percentile(d, 10)), 2),
                            "us_p90": round(1000 * float(np.percentile(d, 90)), 2),
-                           "GBps": round(nbytes_cold[n] / (med * 1e-6) / 1e9, 1),
-                           "frac_of_peak": round(nbytes_cold[n] / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
-    dom = max(["dispatch_recv", "combine"], key=lambda n: kernels[n]["us_mean"])
+                           "GBps": round(nbytes_cold[n] / (mean * 1e-6) / 1e9, 1),
+                           "frac_of_peak": round(nbytes_cold[n] / (mean * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+    # The row kernels' roofline, warm (back-to-back steps: x stays in the
+    # Infinity Cache from one step to the next) and cold (every cache flushed
+    # before the launch).  The cold protocol is the one of record when it
+    # ran; the dominant kernel is the slower row kernel under it.
+    row_roof = {}
+    for n in ("dispatch_recv", "combine"):
+        row_roof[n] = {"bytes": nbytes[n],
+                       "warm": {"us_mean": kernels[n]["us_mean"], "GBps": kernels[n]["GBps"],
+                                "frac": kernels[n]["frac_of_peak"]}}
+        if n in kernels_cold:
+            row_roof[n]["cold"] = {"us_mean": kernels_cold[n]["us_mean"],
+                                   "GBps": kernels_cold[n]["GBps"],
+                                   "frac": kernels_cold[n]["frac_of_peak"]}
+    leg = "cold" if kernels_cold else "warm"
+    dom = max(["dispatch_recv", "combine"], key=lambda n: row_roof[n][leg]["us_mean"])
     if fp8 is not None:
         fp8["speedup_vs_bf16_recv"] = round(kernels["dispatch_recv"]["us_mean"] / fp8["us_mean"], 3)
     step_bytes = sum(nbytes.values())
@@ -432,7 +562,7 @@ def main() -> int:
     copy_gbps = 2 * (1 << 30) * 5 / (a.elapsed_time(b) * 1e-3) / 1e9
     del src, dst
 
-    traffic = measured_traffic(dom, cfg.name)
+    traffic = measured_traffic(dom, cfg.name, cold=leg == "cold")
     rec = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -449,17 +579,19 @@ def main() -> int:
         "config": {"workload": cfg.name, "T": T, "H": H, "E": E, "k": k, "virtual_ranks": R,
                    "local_experts": cfg.L, "capacity": P, "seed": args.seed,
                    "step": "route+dispatch_send+dispatch_recv+combine",
-                   "accumulate": "fp32", "inputs": "resident in HBM"},
+                   "accumulate": "fp32", "inputs": CACHE_STATE["step"]},
         "hbm_GBps_step": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "hbm_frac_step": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": {
             "kernel": dom,
+            "cache": CACHE_STATE[leg],
             "bound": "hbm",
-            "achieved": kernels[dom]["GBps"],
+            "achieved": row_roof[dom][leg]["GBps"],
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": kernels[dom]["frac_of_peak"],
+            "frac": row_roof[dom][leg]["frac"],
             "traffic": traffic,
+            "row_kernels": row_roof,
         },
         "kernels": kernels,
         "kernels_cold": kernels_cold or None,

@@ -24,12 +24,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmoe_route.so)")
 
 
-def command(out: str = LIB) -> list[str]:
+def command(out: str = LIB, defines: tuple = ()) -> list[str]:
+    """hipcc command line; ``defines`` (e.g. ``("MOE_RECV_SLICES=1",)``) build
+    the measurement variants that probes.py compares against the library."""
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # keep the compiler from forming packed fp32 VALU ops
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wall", f"-I{INCLUDE}", "-o", out, SRC,
+        "-Wall", f"-I{INCLUDE}", *[f"-D{d}" for d in defines], "-o", out, SRC,
     ]
 
 
@@ -71,6 +73,29 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     build_c_smoke(verbose)
     return LIB
+
+
+VARIANT_DIR = os.path.join(ROOT, "_build")
+
+
+def variant_path(slices: int) -> str:
+    return os.path.join(VARIANT_DIR, f"recv_slices_{slices}", "libmoe_route.so")
+
+
+def build_variant(slices: int, verbose: bool = False) -> str:
+    """The library with another slice count per recv wave, for measurement
+    only (never loaded by the package)."""
+    out = variant_path(slices)
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    cmd = command(out + ".tmp", (f"MOE_RECV_SLICES={slices}",))
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed ({res.returncode}) building {out}")
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

@@ -45,10 +45,11 @@
 //                        token) and the single-block send in one launch; the
 //                        last block to finish routing, found with a
 //                        device-scope arrival counter, runs the send.
-//   dispatch_recv_kernel one block per (token, 1 KiB column slice); each wave
-//                        copies the slice to one of the token's k rows: a
-//                        cached 16-byte load (the block's waves share it) and
-//                        a non-temporal 16-byte store per lane.
+//   dispatch_recv_kernel one block per (token, two 1 KiB column slices); each
+//                        wave copies both slices to one of the token's k
+//                        rows: two cached 16-byte loads per lane (the block's
+//                        waves share them), both issued before the
+//                        non-temporal 16-byte stores.
 //   dispatch_recv_fp8_kernel
 //                        the same scatter with block-scaled fp8 payloads:
 //                        each 16-lane DPP row holds one 128-element block, so
@@ -170,8 +171,8 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int e, bool valid, int nbi
 }
 
 // In-place exclusive scan of data[0, n) in LDS (n <= 1024); returns the total.
-// Every thread of the block must call it.  scratch: >= 17 ints of LDS.
-__device__ int32_t block_excl_scan(int32_t* data, int n, int32_t* scratch) {
+// Every thread of the block must call it.  tmp: >= 17 ints of LDS.
+__device__ int32_t block_excl_scan(int32_t* data, int n, int32_t* tmp) {
   const int nthreads = blockDim.x;
   const int nwaves = nthreads / kWave;
   const int lane = lane_id();
@@ -182,16 +183,16 @@ __device__ int32_t block_excl_scan(int32_t* data, int n, int32_t* scratch) {
   for (int i = 0; i < per; ++i)
     if (beg + i < n) s += data[beg + i];
   const int32_t incl = wave_incl_scan(s);
-  if (lane == kWave - 1) scratch[wid] = incl;
+  if (lane == kWave - 1) tmp[wid] = incl;
   __syncthreads();
   if (wid == 0) {
-    const int32_t ws = lane < nwaves ? scratch[lane] : 0;
+    const int32_t ws = lane < nwaves ? tmp[lane] : 0;
     const int32_t wi = wave_incl_scan(ws);
-    if (lane < nwaves) scratch[lane] = wi - ws;
-    if (lane == nwaves - 1) scratch[16] = wi;
+    if (lane < nwaves) tmp[lane] = wi - ws;
+    if (lane == nwaves - 1) tmp[16] = wi;
   }
   __syncthreads();
-  int32_t run = scratch[wid] + incl - s;
+  int32_t run = tmp[wid] + incl - s;
   for (int i = 0; i < per; ++i) {
     if (beg + i < n) {
       const int32_t v = data[beg + i];
@@ -199,7 +200,7 @@ __device__ int32_t block_excl_scan(int32_t* data, int n, int32_t* scratch) {
       run += v;
     }
   }
-  const int32_t total = scratch[16];
+  const int32_t total = tmp[16];
   __syncthreads();
   return total;
 }
@@ -757,14 +758,14 @@ __device__ __forceinline__ void send_rank_block(
     int R, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ rank_offsets, int32_t* __restrict__ pair_row,
     int32_t* __restrict__ row_token) {
-  // LDS: [W][E] per-wave counts | [E] base | [17] scratch | [2][THREADS]
+  // LDS: [W][E] per-wave counts | [E] base | [17] scan temporaries | [2][THREADS]
   // partial column sums (multi-block)
   constexpr int nwaves = THREADS / kWave;  // launched with THREADS threads (at most 16 waves)
   const int wid = threadIdx.x / kWave;
   int32_t* hist = sm;
   int32_t* base = sm + nwaves * E;
-  int32_t* scratch = base + E;
-  int32_t* part = scratch + 17;
+  int32_t* scan_tmp = base + E;
+  int32_t* part = scan_tmp + 17;
   int64_t a, b;
   wave_range(P, chunk, bid, a, b);
   // The first step's expert indices are requested before the matrix loads
@@ -886,7 +887,7 @@ __device__ __forceinline__ void send_rank_block(
   }
   __syncthreads();
   // base[e]: total pairs of expert e -> exclusive offsets.
-  const int32_t total = block_excl_scan(base, E, scratch);
+  const int32_t total = block_excl_scan(base, E, scan_tmp);
   if (FUSED || bid == 0) {
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
       offsets[e] = base[e];
@@ -925,7 +926,13 @@ __device__ __forceinline__ void send_rank_block(
         int32_t r = -1;
         if (uint32_t(e) < uint32_t(E)) {
           r = base[e] + my_hist[e] + keep_slot[u];
-          row_token[r] = int32_t(p) / k;
+          // Always below P with a clean histogram matrix; a matrix left
+          // dirty (a workspace not zeroed as documented) drops the pair
+          // instead of storing out of bounds.
+          if (uint64_t(uint32_t(r)) < uint64_t(P))
+            row_token[r] = int32_t(p) / k;
+          else
+            r = -1;
         }
         pair_row[p] = r;
       }
@@ -1007,10 +1014,22 @@ constexpr int kSlice = 64;             // 16-byte chunks per slice: one per lane
 constexpr int kMaxRowThreads = 1024;
 constexpr int64_t kMaxRowBlocks = int64_t(1) << 21;  // beyond this, blocks loop
 
+// Slices of a row one recv wave copies per unit: it issues all their loads
+// before its stores, so each block keeps kRecvSlices KiB of x in flight.
+// Two slices hide the latency of x when it comes from HBM (a cold cache) at
+// no cost when it is cache-resident and the routing spreads over the
+// experts; four are slower either way.  The measurement variants of the
+// other counts are built from this same source with MOE_RECV_SLICES.
+#ifndef MOE_RECV_SLICES
+#define MOE_RECV_SLICES 2
+#endif
+constexpr int kRecvSlices = MOE_RECV_SLICES;
+static_assert(kRecvSlices >= 1 && kRecvSlices <= 8, "slices per recv wave");
+
 struct RecvPlan {
   int groups;  // waves per block; wave g writes destinations g*per .. g*per+per-1
   int per;
-  int ncs;     // slices per row
+  int nsb;     // units (kRecvSlices slices each) per row
   int64_t units;
   unsigned nblocks;
 };
@@ -1019,27 +1038,51 @@ RecvPlan plan_recv(int64_t T, int C, int k) {
   RecvPlan p{};
   p.groups = k < kMaxRowThreads / kSlice ? k : kMaxRowThreads / kSlice;
   p.per = (k + p.groups - 1) / p.groups;
-  p.ncs = (C + kSlice - 1) / kSlice;
-  p.units = T * p.ncs;
+  const int ncs = (C + kSlice - 1) / kSlice;
+  p.nsb = (ncs + kRecvSlices - 1) / kRecvSlices;
+  p.units = T * p.nsb;
   p.nblocks = unsigned(p.units < kMaxRowBlocks ? p.units : kMaxRowBlocks);
   return p;
 }
 
+// Destinations per recv wave: k <= 32 over at most 16 waves.
+constexpr int kRecvMaxPer = kMaxK / (kMaxRowThreads / kSlice);
+
+template <int U>
 __global__ __launch_bounds__(kMaxRowThreads) void dispatch_recv_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ pair_row, int64_t T, int C, int k,
-    int per, int ncs, int64_t units, u32x4* __restrict__ buf, int64_t capacity) {
+    int per, int nsb, int64_t units, u32x4* __restrict__ buf, int64_t capacity) {
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x / kSlice);
   for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
-    const int64_t t = unit / ncs;
-    const int c = int(unit - t * ncs) * kSlice + lane_id();
-    if (c < C) {
-      const u32x4 v = x[t * C + c];  // cached: the block's waves read the same slice
-      for (int jj = 0; jj < per; ++jj) {
-        const int j = g * per + jj;
-        if (j < k) {
-          const int32_t r = pair_row[t * k + j];
-          if (uint64_t(int64_t(r)) < uint64_t(capacity))
-            __builtin_nontemporal_store(v, &buf[int64_t(r) * C + c]);
+    const int64_t t = unit / nsb;
+    const int c0 = int(unit - t * nsb) * (U * kSlice) + lane_id();
+    // Cached loads: the block's waves read the same slices.  Every v[u] is
+    // assigned in every unit, so no value lives across units and nothing
+    // makes the second load wait for the first.
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kSlice;
+      v[u] = c < C ? x[t * C + c] : u32x4{0u, 0u, 0u, 0u};
+    }
+    // The wave's destination rows (uniform: scalar loads), loaded without a
+    // branch (the index is clamped into the token's k entries, and unused
+    // ones are dropped afterwards) so that they are in flight together with
+    // the row loads.
+    int32_t r[kRecvMaxPer];
+#pragma unroll
+    for (int jj = 0; jj < kRecvMaxPer; ++jj) {
+      const int j = g * per + jj;
+      const int32_t v_r = pair_row[t * k + (j < k ? j : k - 1)];
+      r[jj] = jj < per && j < k ? v_r : -1;
+    }
+#pragma unroll
+    for (int jj = 0; jj < kRecvMaxPer; ++jj) {
+      if (uint64_t(int64_t(r[jj])) < uint64_t(capacity)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = c0 + u * kSlice;
+          if (c < C) __builtin_nontemporal_store(v[u], &buf[int64_t(r[jj]) * C + c]);
         }
       }
     }
@@ -1625,8 +1668,8 @@ int enqueue_recv(const void* x, const int32_t* pair_row, int64_t T, int32_t H, i
                  void* buf, int64_t capacity, hipStream_t st) {
   const int C = H / 8;
   const RecvPlan p = plan_recv(T, C, k);
-  return launch(dispatch_recv_kernel, dim3(p.nblocks), dim3(p.groups * kSlice), 0, st,
-                static_cast<const u32x4*>(x), pair_row, T, C, k, p.per, p.ncs, p.units,
+  return launch(dispatch_recv_kernel<kRecvSlices>, dim3(p.nblocks), dim3(p.groups * kSlice), 0,
+                st, static_cast<const u32x4*>(x), pair_row, T, C, k, p.per, p.nsb, p.units,
                 static_cast<u32x4*>(buf), capacity);
 }
 

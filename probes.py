@@ -1,0 +1,288 @@
+"""Measurements behind the shapes of the row kernels, on one MI355X.
+
+    python probes.py recv_slices [--config dsv3_prefill] [--reps 20]
+    python probes.py skew [--reps 20]
+    python probes.py write_fronts [--config dsv3_prefill] [--launches 3]
+    python probes.py cu_scaling [--config dsv3_prefill] [--reps 20]
+
+Each prints one JSON line (write_fronts prints it after its launches, which a
+rocprofv3 --pmc run records per dispatch).
+
+* recv_slices: the recv kernel with 1, 2 and 4 slices (1 KiB column pieces of
+  a token row) per wave, warm (right after a combine, as in back-to-back
+  steps, where x stays in the Infinity Cache) and cold (after a 1 GiB read
+  sweep that evicts every cache).  Slice counts other than the library's
+  come from libraries built from the same source with MOE_RECV_SLICES
+  (``python -m combine_topk_route_amd.build`` builds the product; this script
+  builds the variants under _build/ when they are missing).
+* skew: the same at the DSv3 prefill shape over Zipf-skewed routings, with
+  the effective number of experts n_eff = P^2 / sum_e count_e^2.
+* write_fronts: recv and combine on the workload's routing and on adjacent
+  rows (pair_row[t, j] = t*k + j: each token's k destinations side by side),
+  `launches` times each, in that order: recv real, recv adjacent, combine
+  real, combine adjacent.
+* cu_scaling: recv on streams restricted to n of the chip's CUs
+  (hipExtStreamCreateWithCUMask), n = 32 .. all, CUs taken evenly over the
+  chip or the first n.
+
+All inputs are the seeded synthetic workloads of ``workloads``.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import dataclasses
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+LIB_SLICES = 2  # the library's slices per recv wave (MOE_RECV_SLICES default)
+
+
+def _setup(name, seed=0, zipf_s="config"):
+    import numpy as np
+    import torch
+
+    import combine_topk_route_amd as m
+    import workloads
+
+    cfg = workloads.CONFIGS[name]
+    if zipf_s != "config":
+        cfg = dataclasses.replace(cfg, zipf_s=zipf_s, hot_bias=None, hot_rank=None)
+    wl = workloads.make(cfg, seed=seed)
+    dev = torch.device("cuda:0")
+    d = dict(cfg=cfg,
+             logits=torch.from_numpy(wl.logits).to(dev),
+             x=torch.from_numpy(wl.x.view(np.int16)).view(torch.bfloat16).to(dev),
+             y=torch.from_numpy(wl.y.view(np.int16)).view(torch.bfloat16).to(dev))
+    del wl
+    d["idx"], d["w"] = m.moe_route_topk(d["logits"], cfg.k)
+    d["send"] = m.moe_dispatch_send(d["idx"], cfg.E, cfg.R)
+    d["buf"] = torch.empty((cfg.P, cfg.H), dtype=torch.bfloat16, device=dev)
+    d["out"] = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    c = d["send"].expert_counts.double()
+    d["n_eff"] = float(cfg.P * cfg.P / (c * c).sum())
+    d["active_experts"] = int((c > 0).sum())
+    return d
+
+
+def _recv_variant(slices):
+    """C entry moe_dispatch_recv of the library built with `slices`."""
+    import combine_topk_route_amd as m
+    from combine_topk_route_amd import build as b
+
+    if slices == LIB_SLICES:
+        lib = m._lib.load()
+    else:
+        path = b.variant_path(slices)
+        if not os.path.exists(path):
+            b.build_variant(slices)
+        lib = ctypes.CDLL(path)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        lib.moe_dispatch_recv.argtypes = [vp, vp, i64, i32, i32, vp, i64, vp]
+        lib.moe_dispatch_recv.restype = ctypes.c_int
+    return lib.moe_dispatch_recv
+
+
+class _Timer:
+    def __init__(self, reps, rounds=3):
+        import torch
+
+        self.reps, self.rounds = reps, rounds
+        self.stream = torch.cuda.current_stream()
+        self.flush = torch.empty((1 << 28,), dtype=torch.float32,
+                                 device="cuda").fill_(1.0)  # 1 GiB
+
+    def median_us(self, fn, pre):
+        """Median over rounds of the median of `reps` launches, each after `pre`."""
+        import numpy as np
+        import torch
+
+        meds = []
+        for _ in range(self.rounds):
+            ev = []
+            for _ in range(self.reps):
+                pre()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(self.stream)
+                fn()
+                b.record(self.stream)
+                ev.append((a, b))
+            torch.cuda.synchronize()
+            meds.append(float(np.median([a.elapsed_time(b) * 1000.0 for a, b in ev])))
+        return float(np.median(meds))
+
+    def cold(self):
+        self.flush.amax()
+
+
+def _recv_bytes(cfg):
+    return 2 * cfg.T * cfg.H + 2 * cfg.P * cfg.H + 4 * cfg.P
+
+
+def _slices_rows(d, timer, slices_list):
+    import combine_topk_route_amd as m
+
+    cfg = d["cfg"]
+    st = timer.stream.cuda_stream
+    ref = m.moe_dispatch_recv(d["x"], d["send"].pair_row)
+    comb = lambda: m.moe_combine(d["y"], d["send"].pair_row, d["w"], out=d["out"],
+                                 stream=timer.stream)
+    rows = []
+    for u in slices_list:
+        fn_c = _recv_variant(u)
+        call = lambda: fn_c(d["x"].data_ptr(), d["send"].pair_row.data_ptr(), cfg.T, cfg.H,
+                            cfg.k, d["buf"].data_ptr(), cfg.P, st)
+        d["buf"].zero_()
+        rc = call()
+        import torch
+
+        torch.cuda.synchronize()
+        same = rc == 0 and torch.equal(d["buf"].view(torch.int16), ref.view(torch.int16))
+        warm = timer.median_us(call, comb)
+        cold = timer.median_us(call, timer.cold)
+        nb = _recv_bytes(cfg)
+        rows.append({"slices": u, "library": u == LIB_SLICES, "bit_exact": bool(same),
+                     "warm_us": round(warm, 1), "cold_us": round(cold, 1),
+                     "warm_frac": round(nb / warm / 1e3 / 8000.0, 4),
+                     "cold_frac": round(nb / cold / 1e3 / 8000.0, 4)})
+        print(f"[probe] {cfg.name} slices {u}: warm {warm:.1f} us cold {cold:.1f} us",
+              file=sys.stderr, flush=True)
+    del ref
+    return rows
+
+
+def probe_recv_slices(args):
+    timer = _Timer(args.reps)
+    d = _setup(args.config)
+    rows = _slices_rows(d, timer, (1, 2, 4))
+    return {"probe": "recv_slices", "workload": args.config, "n_eff": round(d["n_eff"], 1),
+            "active_experts": d["active_experts"], "reps": args.reps, "rows": rows}
+
+
+def probe_skew(args):
+    import torch
+
+    timer = _Timer(args.reps)
+    out = []
+    for s in (None, 0.4, 0.8, 1.2):
+        d = _setup("dsv3_prefill", zipf_s=s)
+        rows = _slices_rows(d, timer, (1, 2))
+        out.append({"zipf_s": s, "n_eff": round(d["n_eff"], 1),
+                    "active_experts": d["active_experts"], "rows": rows})
+        del d
+        torch.cuda.empty_cache()
+    return {"probe": "skew", "workload": "dsv3_prefill shape, Zipf routing", "reps": args.reps,
+            "sweep": out}
+
+
+def probe_write_fronts(args):
+    import torch
+
+    import combine_topk_route_amd as m
+
+    d = _setup(args.config)
+    cfg = d["cfg"]
+    adj = torch.arange(cfg.P, dtype=torch.int32, device="cuda").view(cfg.T, cfg.k)
+    pr = d["send"].pair_row
+    st = torch.cuda.current_stream()
+    order = []
+    for kern, rows in (("recv", pr), ("recv", adj), ("combine", pr), ("combine", adj)):
+        for _ in range(args.launches):
+            if kern == "recv":
+                m.moe_dispatch_recv(d["x"], rows, buf=d["buf"], stream=st)
+            else:
+                m.moe_combine(d["y"], rows, d["w"], out=d["out"], stream=st)
+            order.append(f"{kern}_{'real' if rows is pr else 'adjacent'}")
+        torch.cuda.synchronize()
+    return {"probe": "write_fronts", "workload": args.config, "dispatch_order": order}
+
+
+def _hip_runtime():
+    """The HIP runtime torch loaded (the library binds to the same one)."""
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64.so" in line:
+                return ctypes.CDLL(line.split()[-1])
+    raise RuntimeError("libamdhip64 is not loaded")
+
+
+def probe_cu_scaling(args):
+    import torch
+
+    import combine_topk_route_amd as m
+
+    hip = _hip_runtime()
+    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                 ctypes.c_uint32,
+                                                 ctypes.POINTER(ctypes.c_uint32)]
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    d = _setup(args.config)
+    cfg = d["cfg"]
+    timer = _Timer(args.reps)
+    rows = []
+    for layout in ("spread", "first"):
+        for n in sorted({32, 64, 128, 192, ncu}):
+            if n > ncu:
+                continue
+            cus = ([int(i * ncu / n) for i in range(n)] if layout == "spread" else list(range(n)))
+            words = (ctypes.c_uint32 * ((ncu + 31) // 32))()
+            for c in cus:
+                words[c // 32] |= 1 << (c % 32)
+            h = ctypes.c_void_p()
+            rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), len(words), words)
+            if rc != 0:
+                rows.append({"layout": layout, "cus": n, "error": int(rc)})
+                continue
+            s = torch.cuda.ExternalStream(h.value)
+            timer.stream = s
+            with torch.cuda.stream(s):
+                call = lambda: m.moe_dispatch_recv(d["x"], d["send"].pair_row, buf=d["buf"],
+                                                   stream=s)
+                comb = lambda: m.moe_combine(d["y"], d["send"].pair_row, d["w"], out=d["out"],
+                                             stream=s)
+                warm = timer.median_us(call, comb)
+            torch.cuda.synchronize()
+            hip.hipStreamDestroy(h)
+            nb = _recv_bytes(cfg)
+            rows.append({"layout": layout, "cus": n, "warm_us": round(warm, 1),
+                         "GBps": round(nb / warm / 1e3, 1),
+                         "GBps_per_cu": round(nb / warm / 1e3 / n, 2)})
+            print(f"[probe] cu_scaling {layout} {n} CUs: {warm:.1f} us", file=sys.stderr,
+                  flush=True)
+    return {"probe": "cu_scaling", "workload": args.config, "cus_total": ncu, "reps": args.reps,
+            "rows": rows}
+
+
+PROBES = {"recv_slices": probe_recv_slices, "skew": probe_skew,
+          "write_fronts": probe_write_fronts, "cu_scaling": probe_cu_scaling}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("probe", choices=list(PROBES) + ["build"])
+    ap.add_argument("--config", default="dsv3_prefill")
+    ap.add_argument("--reps", type=int, default=20)
+    ap.add_argument("--launches", type=int, default=3)
+    args = ap.parse_args()
+    if args.probe == "build":  # the variant libraries, on a machine with hipcc
+        from combine_topk_route_amd import build as b
+
+        for u in (1, 4):
+            print(b.build_variant(u, verbose=True), flush=True)
+        return 0
+    import torch
+
+    torch.cuda.set_device(0)
+    print(json.dumps(PROBES[args.probe](args)), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -346,7 +346,7 @@ def test_identity_experts_round_trip_and_determinism():
     for bit, except that -0.0 comes back as +0.0 (the accumulator starts at
     +0.0); two runs give identical bytes."""
     m = _m()
-    for name in ["tiny", "mixtral", "dsv3_decode", "kimi_k2"]:
+    for name in ["tiny", "mixtral", "dsv3_decode", "dsv3_prefill", "kimi_k2"]:
         wl = workloads.make(name, seed=1, with_y=False)
         cfg = wl.cfg
         print(f"[edges] identity round trip {name}", flush=True)
@@ -358,11 +358,14 @@ def test_identity_experts_round_trip_and_determinism():
             send, buf = m.moe_dispatch(idx, x, cfg.E, cfg.R)
             out = m.moe_combine(buf, send.pair_row, w)
             torch.cuda.synchronize()
-            outs.append((host(idx), host(w), host(send.pair_row), host_bf16(buf), host_bf16(out)))
+            outs.append([t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+                         for t in (idx, w, send.pair_row, buf, out)])
         expect = np.where(wl.x == 0x8000, np.uint16(0), wl.x)
-        assert np.array_equal(outs[0][4], expect), name
-        for a, b in zip(outs[0], outs[1]):
-            assert np.array_equal(a, b), name
+        assert np.array_equal(host_bf16(outs[0][4].view(torch.bfloat16)), expect), name
+        for a, b in zip(outs[0], outs[1]):  # bytes compared on the device
+            assert torch.equal(a, b), name
+        del outs, buf, out, x
+        torch.cuda.empty_cache()
 
 
 def test_empty_batch_is_a_no_op():
@@ -383,3 +386,53 @@ def test_capacity_errors_raise():
     with pytest.raises(m.MoeError) as ei:
         m.moe_dispatch_recv(x, pr, buf=torch.zeros((7, 64), dtype=torch.bfloat16, device=DEV))
     assert ei.value.status == -3
+
+
+def test_dirty_route_dispatch_workspace_stays_in_bounds():
+    """A moe_route_dispatch workspace that was not zeroed (against the
+    documented contract) gives wrong routing tables but no access out of
+    bounds: every pair_row entry is -1 or below T*k, and the canary entries
+    of row_token and rows of buf past T*k are untouched.  Zeroed again, the
+    same workspace gives the oracle's results."""
+    m = _m()
+    from gpuhelp import assert_step_matches_oracle
+
+    T, E, k, R, H = 4096, 256, 8, 32, 64
+    P = T * k
+    rng = np.random.default_rng(31)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    xb = _rand_bf16((T, H), 32)
+    logits, x = dev_f32(lg), dev_bf16(xb)
+    nws = m.moe_route_dispatch_workspace_bytes(T, E, k)
+    ws = torch.zeros((nws,), dtype=torch.uint8, device=DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    counts = torch.empty((E,), dtype=torch.int32, device=DEV)
+    offsets = torch.empty((E + 1,), dtype=torch.int32, device=DEV)
+    pair_row = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    row_token = torch.full((P + 64,), -7, dtype=torch.int32, device=DEV)
+    rank_off = torch.empty((R + 1,), dtype=torch.int32, device=DEV)
+    buf = torch.full((P + 4, H), 0x3C5A, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    # Small counts shift rows a little (collisions inside [0, P)); large ones
+    # push most rows past P.  Values stay small enough that no sum overflows.
+    for hi in (4, 1 << 15):
+        dirty = rng.integers(0, hi, size=nws // 4, dtype=np.int32)
+        ws.copy_(dev_i32(dirty).view(torch.uint8))
+        print(f"[edges] dirty route_dispatch workspace, counts below {hi}", flush=True)
+        m.moe_route_dispatch(logits, x, k, R, topk_idx=idx, topk_w=w, expert_counts=counts,
+                             expert_offsets=offsets, pair_row=pair_row,
+                             row_token=row_token[:P], rank_offsets=rank_off, buf=buf,
+                             capacity=P + 4, workspace=ws)
+        torch.cuda.synchronize()
+        pr = host(pair_row)
+        assert ((pr >= -1) & (pr < P)).all()
+        assert (host(row_token)[P:] == -7).all()
+        assert (host_bf16(buf)[P:] == 0x3C5A).all()
+    ws.zero_()
+    m.moe_route_dispatch(logits, x, k, R, topk_idx=idx, topk_w=w, expert_counts=counts,
+                         expert_offsets=offsets, pair_row=pair_row, row_token=row_token[:P],
+                         rank_offsets=rank_off, buf=buf, capacity=P + 4, workspace=ws)
+    torch.cuda.synchronize()
+    assert_step_matches_oracle(lg, xb, k, E, R, idx, w,
+                               (counts, offsets, pair_row, row_token[:P], rank_off), buf)
+    assert int(ws.count_nonzero().item()) == 0
