@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     moe_combine,
     moe_dispatch,
     moe_dispatch_fp8,
+    moe_dispatch_noalloc,
     moe_dispatch_recv_fp8,
     moe_dispatch_recv,
     moe_dispatch_send,

@@ -32,6 +32,8 @@ SIGNATURES = {
     "moe_dispatch_fp8": (_c_int, [_vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp,
                                   _vp, _vp, _vp, _vp, _c_i64, _vp, _c_size, _vp]),
     "moe_combine": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i32, _c_i32, _c_i64, _vp, _vp]),
+    "moe_dispatch_noalloc": (_c_int, [_vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _c_i64, _vp]),
     "moe_route_dispatch": (_c_int, [_vp, _vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                     _c_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp,
                                     _c_size, _vp]),

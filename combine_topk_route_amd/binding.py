@@ -260,6 +260,40 @@ def moe_dispatch(topk_idx: torch.Tensor, x: torch.Tensor, E: int, num_vranks: in
     return out, buf
 
 
+def moe_dispatch_noalloc(topk_idx: torch.Tensor, x: torch.Tensor, E: int, num_vranks: int, *,
+                         buf: torch.Tensor, expert_counts: torch.Tensor,
+                         expert_offsets: torch.Tensor, pair_row: torch.Tensor,
+                         row_token: torch.Tensor, rank_offsets: Optional[torch.Tensor] = None,
+                         capacity: Optional[int] = None, stream=None):
+    """moe_dispatch for callers that cannot allocate: every output is the
+    caller's, and the send scratch is the library's own per-device array, so
+    neither this function nor the library allocates anything.  Calls that
+    overlap on one device race on that array.  Returns (SendResult, buf)."""
+    ip = _dev(topk_idx, "topk_idx", torch.int32, 2)
+    d = topk_idx.get_device()
+    xp = _dev(x, "x", torch.bfloat16, 2, device=d)
+    T, k = topk_idx.shape
+    H = x.shape[1]
+    if x.shape[0] != T:
+        raise ValueError("x and topk_idx disagree on T")
+    out = SendResult(expert_counts, expert_offsets, pair_row, row_token, rank_offsets)
+    sizes = [(expert_counts, E), (expert_offsets, E + 1), (pair_row, T * k), (row_token, T * k)]
+    if rank_offsets is not None:
+        sizes.append((rank_offsets, num_vranks + 1))
+    for t, n in sizes:
+        if t.numel() != n:
+            raise ValueError("dispatch output has the wrong number of elements")
+    if capacity is None:
+        capacity = buf.shape[0]
+    if buf.dim() != 2 or buf.shape[1] != H or buf.shape[0] < capacity:
+        raise ValueError("buf must be [>= capacity, H]")
+    cp, op, pp, tp, rp = _send_ptrs(out, d)
+    _check("moe_dispatch_noalloc", _lib.load().moe_dispatch_noalloc(
+        ip, xp, T, E, k, H, num_vranks, cp, op, pp, tp, rp,
+        _dev(buf, "buf", torch.bfloat16, device=d), capacity, _stream(stream, x)))
+    return out, buf
+
+
 def moe_route_dispatch_workspace_bytes(T: int, E: int, k: int) -> int:
     return int(_lib.load().moe_route_dispatch_workspace_bytes(T, E, k))
 

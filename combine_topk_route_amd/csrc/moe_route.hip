@@ -71,6 +71,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
 #include <tuple>
 #include <utility>
 
@@ -1815,6 +1817,52 @@ int enqueue_route_and_send(const float* logits, int64_t T, int32_t E, int32_t k,
                             rank_offsets, mat, rank_arrivals, s);
 }
 
+// ---------------------------------------------------------------------------
+// scratch of moe_dispatch_noalloc: the send histogram matrix in device memory
+// the library owns, for callers that cannot allocate
+// ---------------------------------------------------------------------------
+
+constexpr size_t kScratchBytes = size_t(kSendMatrixInts) * sizeof(int32_t);  // 64 KiB
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+// One copy per device, held until the process ends.  In host code the name
+// stands for a host-side shadow, not a device address: kernels receive the
+// address hipGetSymbolAddress returns for the device, never `scratch` itself.
+static __device__ __align__(256) int32_t scratch[kSendMatrixInts];
+
+namespace {
+
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the device that owns `st`, looked up once
+// per device with that device current (each device holds its own copy at
+// its own address).
+int scratch_address(hipStream_t st, void** addr) {
+  int dev = -1;
+  const hipError_t e0 = st == nullptr ? hipGetDevice(&dev) : hipStreamGetDevice(st, &dev);
+  if (e0 != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_INVALID_ARG;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      int cur = -1;
+      if (hipGetDevice(&cur) != hipSuccess) return MOE_ERR_HIP;
+      if (cur != dev && hipSetDevice(dev) != hipSuccess) return MOE_ERR_HIP;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (cur != dev && hipSetDevice(cur) != hipSuccess) return MOE_ERR_HIP;
+      if (e != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *addr = p;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1893,6 +1941,25 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int64_t T, int32_t E, i
                     row_token, rank_offsets, workspace, s);
   if (st != MOE_OK) return st;
   return enqueue_recv(x, pair_row, T, H, k, buf, capacity, s);
+}
+
+int moe_dispatch_noalloc(const int32_t* topk_idx, const void* x, int64_t T, int32_t E,
+                         int32_t k, int32_t H, int32_t num_vranks, int32_t* expert_counts,
+                         int32_t* expert_offsets, int32_t* pair_row, int32_t* row_token,
+                         int32_t* rank_offsets, void* buf, int64_t capacity, void* stream) {
+  const int st = check_route_shape(T, E, k);
+  if (st != MOE_OK) return st;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  const size_t need = T > 0 ? plan_send(T * k, E).ws_bytes : 0;
+  if (need > kScratchBytes) return MOE_ERR_WORKSPACE;  // never above 64 KiB by the send plan
+  if (need > 0) {
+    const int rc = scratch_address(static_cast<hipStream_t>(stream), &ws);
+    if (rc != MOE_OK) return rc;
+    ws_bytes = kScratchBytes;
+  }
+  return moe_dispatch(topk_idx, x, T, E, k, H, num_vranks, expert_counts, expert_offsets, pair_row,
+                      row_token, rank_offsets, buf, capacity, ws, ws_bytes, stream);
 }
 
 size_t moe_route_dispatch_workspace_bytes(int64_t T, int32_t E, int32_t k) {

@@ -22,7 +22,9 @@
  * ---------------------------------------
  *  - Every data pointer is a DEVICE pointer owned by the caller (for
  *    instance a torch tensor's data_ptr()).  The library allocates and frees
- *    nothing and keeps no global state; it is reentrant.
+ *    nothing and is reentrant.  Its only global state is the per-device
+ *    scratch array of moe_dispatch_noalloc (for callers that cannot
+ *    allocate); every other entry point uses caller memory only.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Calls only enqueue work on it; none synchronises the device or copies
  *    device -> host.  Stream order is the only synchronisation: results are
@@ -195,6 +197,30 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int64_t T, int32_t E,
                  int32_t* pair_row, int32_t* row_token, int32_t* rank_offsets,
                  void* buf, int64_t capacity, void* workspace,
                  size_t workspace_bytes, void* stream);
+
+/*
+ * moe_dispatch_noalloc - moe_dispatch for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments without the
+ * workspace, the same kernels and results.  The multi-block send keeps its
+ * [blocks][E] count matrix in a device array the library owns instead:
+ * 64 KiB per device, held on each device the library runs on until the
+ * process ends (the send plan never needs more; a larger need would return
+ * MOE_ERR_WORKSPACE).  Nothing is allocated; the first call on a device
+ * looks up that device's copy of the array (hipGetSymbolAddress) once.
+ * Every call on one device shares that device's array and the kernels
+ * overwrite the part they use, so nothing needs clearing, but calls that
+ * overlap on one device (different streams, or different threads without
+ * ordering) race on it and must not be made.
+ * Errors: as moe_dispatch, plus MOE_ERR_HIP if the device or its array
+ *         cannot be looked up.
+ */
+int moe_dispatch_noalloc(const int32_t* topk_idx, const void* x, int64_t T,
+                         int32_t E, int32_t k, int32_t H, int32_t num_vranks,
+                         int32_t* expert_counts, int32_t* expert_offsets,
+                         int32_t* pair_row, int32_t* row_token,
+                         int32_t* rank_offsets, void* buf, int64_t capacity,
+                         void* stream);
 
 /*
  * moe_route_dispatch - moe_route_topk, moe_dispatch_send and
