@@ -437,7 +437,11 @@ def main() -> int:
         route_grouped = {"n_group": n_group, "topk_group": topk_group, "us_mean": round(us, 2),
                          "bytes": gb, "GBps": round(gb / (us * 1e-6) / 1e9, 1),
                          "frac_of_peak": round(gb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-                         "alu": alu_roofline("route_grouped", us, cfg.name)}
+                         "alu": None}
+        g_trace = _committed_count(TRACE_FILE, "route_grouped", cfg.name)
+        if g_trace is not None:
+            a_ = alu_roofline("route_grouped", g_trace, cfg.name)
+            route_grouped["alu"] = None if a_ is None else dict(a_, us_trace=g_trace)
         # the headline's routing outputs again, for anything timed after this
         m.moe_route_topk(logits, k, topk_idx=idx, topk_w=w, stream=stream)
         torch.cuda.synchronize()
@@ -503,19 +507,24 @@ def main() -> int:
                       "us_p90": round(1000 * float(np.percentile(per[n], 90)), 2),
                       "bytes": nbytes[n], "GBps": round(gbps, 1),
                       "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    # Routing's ALU roofline: VALU issue time over the kernel's own duration,
+    # the committed kernel trace's average for the same code (an event pair
+    # per launch adds record overhead of the kernel's own size, and
+    # back-to-back graph replay a launch gap of about a microsecond per
+    # kernel; the live back-to-back figure is reported beside it).  The
+    # counting kernel of the headline step runs inside moe_route_dispatch,
+    # where no event can bracket it.
     if route_b2b_us is not None:
         kernels["route"]["us_back_to_back"] = round(route_b2b_us, 2)
-    kernels["route"]["alu"] = alu_roofline(
-        "route", route_b2b_us if route_b2b_us is not None else kernels["route"]["us_mean"],
-        cfg.name)
-    # The counting routing kernel of the headline step runs inside
-    # moe_route_dispatch, where no event can bracket it: its time is the
-    # committed kernel trace's average for the same code.
-    trace_us = _committed_count(TRACE_FILE, "route_counting", cfg.name)
-    if trace_us is not None:
-        a_ = alu_roofline("route_counting", trace_us, cfg.name)
-        if a_ is not None:
-            kernels["route"]["alu_counting"] = dict(a_, us_trace=trace_us)
+    for key, name in (("alu", "route"), ("alu_counting", "route_counting")):
+        trace_us = _committed_count(TRACE_FILE, name, cfg.name)
+        if trace_us is not None:
+            a_ = alu_roofline(name, trace_us, cfg.name)
+            if a_ is not None:
+                kernels["route"][key] = dict(a_, us_trace=trace_us)
+                if name == "route" and route_b2b_us is not None:
+                    kernels["route"][key]["frac_back_to_back"] = round(
+                        a_["issue_us"] / route_b2b_us, 4)
     nbytes_cold = dict(nbytes, dispatch=nbytes["dispatch_send"] + nbytes["dispatch_recv"])
     kernels_cold = {}
     for n in cold_names:
