@@ -4,6 +4,7 @@
     python probes.py skew [--reps 20]
     python probes.py write_fronts [--config dsv3_prefill] [--launches 3]
     python probes.py cu_scaling [--config dsv3_prefill] [--reps 20]
+    python probes.py overlap_masked [--config dsv3_prefill] [--reps 20]
 
 Each prints one JSON line (write_fronts prints it after its launches, which a
 rocprofv3 --pmc run records per dispatch).
@@ -24,6 +25,9 @@ rocprofv3 --pmc run records per dispatch).
 * cu_scaling: recv on streams restricted to n of the chip's CUs
   (hipExtStreamCreateWithCUMask), n = 32 .. all, CUs taken evenly over the
   chip or the first n.
+* overlap_masked: dispatch beside the stand-in shared-expert GEMM, back to
+  back, on two unmasked streams, and with the CUs split between two masked
+  streams.
 
 All inputs are the seeded synthetic workloads of ``workloads``.
 """
@@ -260,8 +264,105 @@ def probe_cu_scaling(args):
             "rows": rows}
 
 
+def _masked_stream(hip, ncu, first, count):
+    """A default-priority stream restricted to CU mask bits [first, first + count)."""
+    words = (ctypes.c_uint32 * ((ncu + 31) // 32))()
+    for c in range(first, first + count):
+        words[c // 32] |= 1 << (c % 32)
+    h = ctypes.c_void_p()
+    rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), len(words), words)
+    return (h, rc)
+
+
+def probe_overlap_masked(args):
+    """Dispatch (send + recv) beside the stand-in shared-expert GEMM of
+    bench.py's overlap leg, x[T, H] @ W[H, 2048] in bf16: back to back on the
+    whole chip, concurrently on two unmasked streams, and concurrently with
+    the CUs split between them (dispatch on mask bits [0, n), the GEMM on
+    [n, all))."""
+    import numpy as np
+    import torch
+
+    import combine_topk_route_amd as m
+
+    hip = _hip_runtime()
+    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                 ctypes.c_uint32,
+                                                 ctypes.POINTER(ctypes.c_uint32)]
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    d = _setup(args.config)
+    cfg = d["cfg"]
+    wsh = torch.randn((cfg.H, 2048), device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    gout = torch.empty((cfg.T, 2048), dtype=torch.bfloat16, device="cuda")
+    main = torch.cuda.current_stream()
+
+    def disp(st):
+        m.moe_dispatch(d["idx"], d["x"], cfg.E, cfg.R, buf=d["buf"], stream=st)
+
+    def gemm(st):
+        with torch.cuda.stream(st):
+            torch.matmul(d["x"], wsh, out=gout)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        res = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(main)
+            fn()
+            b.record(main)
+            torch.cuda.synchronize()
+            res.append(a.elapsed_time(b) * 1000.0)
+        return float(np.median(res))
+
+    def both(s1, s2):
+        def fn():
+            e = torch.cuda.Event()
+            e.record(main)
+            s1.wait_event(e)
+            s2.wait_event(e)
+            disp(s1)
+            gemm(s2)
+            main.wait_stream(s1)
+            main.wait_stream(s2)
+        return fn
+
+    reps = args.reps
+    t_d = timed(lambda: disp(main), reps)
+    t_g = timed(lambda: gemm(main), reps)
+    other1, other2 = torch.cuda.Stream(), torch.cuda.Stream()
+    t_b = timed(both(other1, other2), reps)
+    rows = [{"split": "none (back to back)", "us": round(t_d + t_g, 1)},
+            {"split": "two unmasked streams", "us": round(t_b, 1)}]
+    for n in (64, 96, 128, 160, 192):
+        h1, rc1 = _masked_stream(hip, ncu, 0, n)
+        h2, rc2 = _masked_stream(hip, ncu, n, ncu - n)
+        if rc1 != 0 or rc2 != 0:
+            rows.append({"split": f"{n} / {ncu - n} CUs", "error": [int(rc1), int(rc2)]})
+            for h, rc in ((h1, rc1), (h2, rc2)):
+                if rc == 0:
+                    hip.hipStreamDestroy(h)
+            continue
+        s1, s2 = torch.cuda.ExternalStream(h1.value), torch.cuda.ExternalStream(h2.value)
+        t_d1 = timed(lambda: (s1.wait_stream(main), disp(s1), main.wait_stream(s1)), reps)
+        t_g2 = timed(lambda: (s2.wait_stream(main), gemm(s2), main.wait_stream(s2)), reps)
+        t_both = timed(both(s1, s2), reps)
+        torch.cuda.synchronize()
+        hip.hipStreamDestroy(h1)
+        hip.hipStreamDestroy(h2)
+        rows.append({"split": f"{n} / {ncu - n} CUs", "dispatch_alone_us": round(t_d1, 1),
+                     "gemm_alone_us": round(t_g2, 1), "us": round(t_both, 1)})
+        print(f"[probe] overlap split {n}/{ncu - n}: {t_both:.1f} us", file=sys.stderr, flush=True)
+    return {"probe": "overlap_masked", "workload": args.config, "cus_total": ncu,
+            "dispatch_us": round(t_d, 1), "gemm_us": round(t_g, 1),
+            "gemm": f"[{cfg.T},{cfg.H}] x [{cfg.H},2048] bf16", "reps": reps, "rows": rows}
+
+
 PROBES = {"recv_slices": probe_recv_slices, "skew": probe_skew,
-          "write_fronts": probe_write_fronts, "cu_scaling": probe_cu_scaling}
+          "write_fronts": probe_write_fronts, "cu_scaling": probe_cu_scaling,
+          "overlap_masked": probe_overlap_masked}
 
 
 def main() -> int:
