@@ -237,7 +237,7 @@ def main() -> int:
     del wl
     # One set of preallocated buffers (the allocation-free API a serving loop
     # uses); the per-entry-point breakdown below writes into the same tensors.
-    bufs = m.MoeBuffers(T, H, E, k, R, device=dev)
+    bufs = m.MoeBuffers(T, H, E, k, R, device=dev, fp8=H % 128 == 0)
     idx, w = bufs.topk_idx, bufs.topk_w
     counts, offsets, rank_off = bufs.expert_counts, bufs.expert_offsets, bufs.rank_offsets
     pair_row, row_token = bufs.pair_row, bufs.row_token
@@ -393,28 +393,66 @@ def main() -> int:
     torch.cuda.synchronize()
     del flush
 
-    # Block-scaled fp8 dispatch recv (same routing; codes + fp32 scales per
-    # 128 elements), timed on its own with an event pair per launch.
+    # Block-scaled fp8 dispatch, the pages' own dispatch payload (codes and
+    # one fp32 scale per 128 elements; combine stays 16-bit): the recv alone,
+    # warm and after the cache sweep, and the whole step with it.
     fp8 = None
     if H % 128 == 0:
-        buf_q = torch.empty((P, H), dtype=torch.uint8, device=dev)
-        buf_s = torch.empty((P, H // 128), dtype=torch.float32, device=dev)
-        m.moe_dispatch_recv_fp8(x, pair_row, buf_q=buf_q, buf_scale=buf_s, stream=stream)
+        buf_q, buf_s = bufs.buf_q, bufs.buf_scale
+        fp8_call = lambda: m.moe_dispatch_recv_fp8(x, pair_row, buf_q=buf_q, buf_scale=buf_s,
+                                                   stream=stream)
+        fp8_call()
+        flush = (torch.empty((1 << 28,), dtype=torch.float32, device=dev).fill_(1.0)
+                 if not args.no_cold else None)
         fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps if flush is not None else 0)]
         torch.cuda.synchronize()
         for a_, b_ in fev:
             a_.record(stream)
-            m.moe_dispatch_recv_fp8(x, pair_row, buf_q=buf_q, buf_scale=buf_s, stream=stream)
+            fp8_call()
+            b_.record(stream)
+        for a_, b_ in cev:
+            flush.amax()
+            a_.record(stream)
+            fp8_call()
             b_.record(stream)
         torch.cuda.synchronize()
-        us = 1000.0 * float(np.mean([a_.elapsed_time(b_) for a_, b_ in fev]))
+        del flush
         fb = 2 * T * H + P * H + 4 * P * (H // 128) + 4 * P
-        fp8 = {"us_mean": round(us, 2), "bytes": fb, "GBps": round(fb / (us * 1e-6) / 1e9, 1),
-               "frac_of_peak": round(fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-               "traffic": measured_traffic("fp8_dispatch_recv", cfg.name),
-               "speedup_vs_bf16_recv": None}
-        del buf_q, buf_s
+
+        def leg(evl):
+            us_ = 1000.0 * float(np.mean([a_.elapsed_time(b_) for a_, b_ in evl]))
+            return {"us_mean": round(us_, 2), "GBps": round(fb / (us_ * 1e-6) / 1e9, 1),
+                    "frac_of_peak": round(fb / (us_ * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+        fp8 = dict(leg(fev), bytes=fb, traffic=measured_traffic("fp8_dispatch_recv", cfg.name),
+                   speedup_vs_bf16_recv=None, cold=leg(cev) if cev else None)
+
+        def step_fp8():
+            _, tw, send, _, _ = bufs.route_dispatch_fp8(logits, x, stream=stream)
+            bufs.combine(y, send.pair_row, tw, stream=stream)
+
+        for _ in range(max(1, args.warmup)):
+            step_fp8()
+        torch.cuda.synchronize()
+        sa, sb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        sa.record(stream)
+        for _ in range(args.steps):
+            step_fp8()
+        sb.record(stream)
+        torch.cuda.synchronize()
+        ms_fp8 = sa.elapsed_time(sb) / args.steps
+        fp8["step"] = {"ms_per_step": round(ms_fp8, 4),
+                       "tokens_per_s": round(T / (ms_fp8 * 1e-3), 1),
+                       "what": "moe_route_dispatch_fp8 + moe_combine (bf16 y), back to back"}
+        # the headline's routing tables again, for anything timed after this
+        m.moe_route_topk(logits, k, topk_idx=idx, topk_w=w, stream=stream)
+        m.moe_dispatch_send(idx, E, R, expert_counts=counts, expert_offsets=offsets,
+                            pair_row=pair_row, row_token=row_token, rank_offsets=rank_off,
+                            workspace=ws, stream=stream)
+        torch.cuda.synchronize()
 
     # Group-limited routing (DeepSeek-V3's grouping: 8 groups of E/8 experts,
     # the 4 best kept) on the same logits, timed on its own like fp8 above.
