@@ -1947,11 +1947,16 @@ int moe_dispatch_noalloc(const int32_t* topk_idx, const void* x, int64_t T, int3
                          int32_t k, int32_t H, int32_t num_vranks, int32_t* expert_counts,
                          int32_t* expert_offsets, int32_t* pair_row, int32_t* row_token,
                          int32_t* rank_offsets, void* buf, int64_t capacity, void* stream) {
-  const int st = check_route_shape(T, E, k);
-  if (st != MOE_OK) return st;
+  // Every argument is checked before the device's scratch is looked up; the
+  // workspace check of the send half is the one failure expected here.
+  int st = check_send(topk_idx, T, E, k, num_vranks, expert_counts, expert_offsets, pair_row,
+                      row_token, rank_offsets, nullptr, 0);
+  if (st != MOE_OK && st != MOE_ERR_WORKSPACE) return st;
+  st = check_rows(T, H, k, capacity, x, buf);
+  if (st != MOE_OK || T == 0) return st;
   void* ws = nullptr;
   size_t ws_bytes = 0;
-  const size_t need = T > 0 ? plan_send(T * k, E).ws_bytes : 0;
+  const size_t need = plan_send(T * k, E).ws_bytes;
   if (need > kScratchBytes) return MOE_ERR_WORKSPACE;  // never above 64 KiB by the send plan
   if (need > 0) {
     const int rc = scratch_address(static_cast<hipStream_t>(stream), &ws);

@@ -9,7 +9,9 @@
  *                     exclusive scan, pair_row is a bijection onto [0, T*k)
  *                     with row_token as its inverse, every dispatched row is
  *                     a bit copy of its token, and combine over the dispatched
- *                     rows (identity experts) returns the input.
+ *                     rows (identity experts) returns the input; then
+ *                     moe_route_dispatch and moe_dispatch_noalloc against the
+ *                     separate calls, byte for byte.
  */
 #include <stdint.h>
 #include <stdio.h>
@@ -45,6 +47,10 @@ static void host_checks(void) {
                            32, NULL, 0, NULL) == MOE_ERR_WORKSPACE);
   CHECK(moe_route_dispatch(p16, p16, 16, 8, 2, 3, 1, 256, 1, p16, p16, p16, p16, p16, p16, NULL, p16,
                            32, p16, 256, NULL) == MOE_ERR_INVALID_ARG); /* E % n_group != 0 */
+  CHECK(moe_dispatch_noalloc(p16, p16, 16, 8, 2, 256, 1, p16, p16, p16, p16, NULL, p16, 31, NULL) ==
+        MOE_ERR_CAPACITY);
+  CHECK(moe_dispatch_noalloc(NULL, NULL, 0, 8, 2, 256, 1, NULL, NULL, NULL, NULL, NULL, NULL, 0,
+                             NULL) == MOE_OK);
 }
 
 static uint16_t bf16_of(float f) { /* round to nearest even */
@@ -162,6 +168,67 @@ static void gpu_checks(void) {
     free(i2); free(r2); free(b2); free(wsh);
     hipFree(d_w2); hipFree(d_idx2); hipFree(d_counts2); hipFree(d_off2); hipFree(d_pr2);
     hipFree(d_rt2); hipFree(d_roff2); hipFree(d_buf2); hipFree(d_ws2);
+  }
+
+  /* moe_dispatch_noalloc on a batch that needs the multi-block send (its
+     scratch in the library's own device array), twice: the same bytes as
+     moe_dispatch with a caller workspace. */
+  {
+    enum { T2 = 2048, E2 = 64, K2 = 4, H2 = 64, R2 = 8, P2 = T2 * K2 };
+    float* lg2 = malloc(sizeof(float) * T2 * E2);
+    uint16_t* x2 = malloc(2 * T2 * H2);
+    for (int i = 0; i < T2 * E2; ++i) {
+      s = s * 1664525u + 1013904223u;
+      lg2[i] = (float)((s >> 8) & 0xFFFF) / 4096.0f - 8.0f;
+    }
+    for (int i = 0; i < T2 * H2; ++i) {
+      s = s * 1664525u + 1013904223u;
+      x2[i] = bf16_of((float)((int)(s >> 16) - 32768) / 8192.0f);
+    }
+    float *d_lg, *d_wt;
+    int32_t *d_id, *d_c[2], *d_o[2], *d_p[2], *d_r[2], *d_ro[2];
+    void *d_xx, *d_b[2], *d_wsp;
+    const size_t wsb2 = moe_dispatch_workspace_bytes(T2, E2, K2);
+    CHECK(wsb2 > 0);
+    HIPCHECK(hipMalloc((void**)&d_lg, sizeof(float) * T2 * E2));
+    HIPCHECK(hipMalloc((void**)&d_wt, sizeof(float) * P2));
+    HIPCHECK(hipMalloc((void**)&d_id, sizeof(int32_t) * P2));
+    HIPCHECK(hipMalloc(&d_xx, 2 * T2 * H2));
+    HIPCHECK(hipMalloc(&d_wsp, wsb2));
+    for (int v = 0; v < 2; ++v) {
+      HIPCHECK(hipMalloc((void**)&d_c[v], sizeof(int32_t) * E2));
+      HIPCHECK(hipMalloc((void**)&d_o[v], sizeof(int32_t) * (E2 + 1)));
+      HIPCHECK(hipMalloc((void**)&d_p[v], sizeof(int32_t) * P2));
+      HIPCHECK(hipMalloc((void**)&d_r[v], sizeof(int32_t) * P2));
+      HIPCHECK(hipMalloc((void**)&d_ro[v], sizeof(int32_t) * (R2 + 1)));
+      HIPCHECK(hipMalloc(&d_b[v], 2 * (size_t)P2 * H2));
+    }
+    HIPCHECK(hipMemcpy(d_lg, lg2, sizeof(float) * T2 * E2, hipMemcpyHostToDevice));
+    HIPCHECK(hipMemcpy(d_xx, x2, 2 * T2 * H2, hipMemcpyHostToDevice));
+    CHECK(moe_route_topk(d_lg, T2, E2, K2, d_id, d_wt, NULL) == MOE_OK);
+    CHECK(moe_dispatch(d_id, d_xx, T2, E2, K2, H2, R2, d_c[0], d_o[0], d_p[0], d_r[0], d_ro[0],
+                       d_b[0], P2, d_wsp, wsb2, NULL) == MOE_OK);
+    for (int rep = 0; rep < 2; ++rep)
+      CHECK(moe_dispatch_noalloc(d_id, d_xx, T2, E2, K2, H2, R2, d_c[1], d_o[1], d_p[1], d_r[1],
+                                 d_ro[1], d_b[1], P2, NULL) == MOE_OK);
+    HIPCHECK(hipDeviceSynchronize());
+    const size_t sizes[6] = {sizeof(int32_t) * E2, sizeof(int32_t) * (E2 + 1), sizeof(int32_t) * P2,
+                             sizeof(int32_t) * P2, sizeof(int32_t) * (R2 + 1), 2 * (size_t)P2 * H2};
+    unsigned char* h0 = malloc(sizes[5]);
+    unsigned char* h1 = malloc(sizes[5]);
+    void* a0[6] = {d_c[0], d_o[0], d_p[0], d_r[0], d_ro[0], d_b[0]};
+    void* a1[6] = {d_c[1], d_o[1], d_p[1], d_r[1], d_ro[1], d_b[1]};
+    for (int i = 0; i < 6; ++i) {
+      HIPCHECK(hipMemcpy(h0, a0[i], sizes[i], hipMemcpyDeviceToHost));
+      HIPCHECK(hipMemcpy(h1, a1[i], sizes[i], hipMemcpyDeviceToHost));
+      CHECK(memcmp(h0, h1, sizes[i]) == 0);
+    }
+    free(h0); free(h1); free(lg2); free(x2);
+    hipFree(d_lg); hipFree(d_wt); hipFree(d_id); hipFree(d_xx); hipFree(d_wsp);
+    for (int v = 0; v < 2; ++v) {
+      hipFree(d_c[v]); hipFree(d_o[v]); hipFree(d_p[v]); hipFree(d_r[v]); hipFree(d_ro[v]);
+      hipFree(d_b[v]);
+    }
   }
 
   long total = 0;

@@ -259,3 +259,25 @@ def test_route_dispatch_fp8_checks_every_part_before_enqueueing(lib):
     assert call(a20=ws - 1) == WS                  # short workspace
     assert call(a2=0, a0=None, a1=None, a9=None, a10=None, a11=None, a12=None, a13=None,
                 a14=None, a16=None, a17=None, a18=0, a19=None, a20=0) == OK
+
+
+def test_noalloc_dispatch_checks_every_argument_before_the_device(lib):
+    """moe_dispatch_noalloc validates every argument before it looks up the
+    device's scratch array, so each bad call fails with its own status (here,
+    with no GPU, a call that passed the checks would fail with MOE_ERR_HIP)."""
+    f = lib.moe_dispatch_noalloc
+    base = [P16, P16, 8192, 256, 8, 7168, 32, P16, P16, P16, P16, None, P16, 8192 * 8, S]
+    cases = [(0, 0, INVALID), (1, 0, INVALID), (13, 8192 * 8 - 1, CAP), (6, 5, INVALID), (5, 7170, ALIGN), (3, 0, INVALID),
+             (4, 33, INVALID), (7, 0, INVALID), (12, 0, INVALID), (12, P4, ALIGN), (2, -1, INVALID)]
+    for i, v, want in cases:
+        args = list(base)
+        args[i] = v
+        assert f(*args) == want, (i, v)
+    zero = list(base)
+    zero[2] = 0
+    assert f(*zero) == OK                          # T == 0: nothing to do, no device needed
+    small = list(base)
+    small[2], small[13] = 16, 16 * 8               # T*k <= 4096 needs no scratch
+    small[5] = 7170
+    assert f(*small) == ALIGN
+    assert f(*base) == HIP                         # valid arguments, but no device here
