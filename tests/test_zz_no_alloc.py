@@ -62,3 +62,64 @@ def test_noalloc_dispatch_matches_workspace_dispatch_and_oracle():
         assert np.array_equal(host(got["pair_row"]), pr)
         assert np.array_equal(host(got["row_token"]), rt)
         assert np.array_equal(host_bf16(got["buf"]), oracle.dispatch_rows(x_bits, pr, T * k))
+
+
+def test_noalloc_dispatch_in_a_graph():
+    """The use the entry point is for: captured into a HIP graph (after one
+    eager call, which looks up the device's scratch array), replayed three
+    times with eager work between replays and once more on new inputs,
+    allocating nothing; every replay matches the oracle."""
+    import combine_topk_route_amd as m
+
+    T, E, k, H, R = 4096, 256, 8, 128, 32
+    rng = np.random.default_rng(12)
+
+    def inputs():
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        xb = rng.integers(0, 1 << 16, size=(T, H), dtype=np.uint16)
+        xb[(xb & 0x7F80) == 0x7F80] = 0x3F80
+        return idx, xb
+
+    idx, xb = inputs()
+    d_idx, d_x = dev_i32(idx), dev_bf16(xb)
+    got = _outputs(T, E, k, H, R)
+    main = torch.cuda.current_stream()
+    m.moe_dispatch_noalloc(d_idx, d_x, E, R, **got)
+    side = torch.cuda.Stream()
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        m.moe_dispatch_noalloc(d_idx, d_x, E, R, stream=side, **got)
+    main.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        m.moe_dispatch_noalloc(d_idx, d_x, E, R, stream=torch.cuda.current_stream(), **got)
+    torch.cuda.synchronize()
+
+    def check(idx_, xb_):
+        pr, rt = oracle.dispatch_slots(idx_, E)
+        counts = oracle.expert_counts(idx_, E)
+        off = oracle.expert_offsets(counts)
+        assert np.array_equal(host(got["expert_counts"]), counts)
+        assert np.array_equal(host(got["expert_offsets"]), off)
+        assert np.array_equal(host(got["rank_offsets"]), oracle.rank_offsets(off, R))
+        assert np.array_equal(host(got["pair_row"]), pr)
+        assert np.array_equal(host(got["row_token"]), rt)
+        assert np.array_equal(host_bf16(got["buf"]), oracle.dispatch_rows(xb_, pr, T * k))
+
+    before = torch.cuda.memory_allocated()
+    for rep in range(3):
+        print(f"[noalloc] graph replay {rep}", flush=True)
+        for name, t in got.items():
+            (t.view(torch.int16) if t.dtype == torch.bfloat16 else t).fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check(idx, xb)
+    idx2, xb2 = inputs()
+    d_idx.copy_(dev_i32(idx2))
+    d_x.copy_(dev_bf16(xb2))
+    g.replay()
+    torch.cuda.synchronize()
+    check(idx2, xb2)
+    assert torch.cuda.memory_allocated() == before
