@@ -60,8 +60,11 @@
 //                        non-temporal 16-byte row loads in flight, fp32 fma
 //                        chain in j order, one bf16 RNE (v_cvt_pk_bf16_f32).
 //                        The token's rows and weights come through the scalar
-//                        cache into SGPRs.  For k = 1, 2, 4 a wave covers
-//                        several slices so that 16 row loads are in flight.
+//                        cache into SGPRs.  k = 1, 2, 4, 8 run
+//                        combine_small_k_kernel, which loads them all before
+//                        issuing its row loads back to back; for k < 8 a wave
+//                        covers several slices so that 16 row loads are in
+//                        flight.
 //
 // There is no dense contraction here, so no MFMA: the row kernels are bound by
 // HBM bandwidth and the routing / send kernels by latency.
@@ -1129,6 +1132,14 @@ __global__ __launch_bounds__(kSendThreads) void send_recv_kernel(
     const int64_t t = unit / nparts;
     const int sp = int(unit - t * nparts);
     const int64_t pt = t * k;  // flat index of the token's first pair
+    // The token's slices do not depend on the routing: their loads go out
+    // first and arrive while the block counts its rows.
+    u32x4 v[kSendRecvSlices];
+#pragma unroll
+    for (int s = 0; s < kSendRecvSlices; ++s) {
+      const int c = (sp * kSendRecvSlices + s) * kSlice + lane;
+      v[s] = wid < k && c < C ? x[t * C + c] : u32x4{0u, 0u, 0u, 0u};
+    }
     int ej[kSendRecvMaxK];
 #pragma unroll
     for (int j = 0; j < kSendRecvMaxK; ++j) ej[j] = j < k ? idx[pt + j] : -1;
@@ -1167,12 +1178,6 @@ __global__ __launch_bounds__(kSendThreads) void send_recv_kernel(
     if (wid < k) {
       const int32_t r = rows[wid];
       if (uint64_t(int64_t(r)) < uint64_t(capacity)) {
-        u32x4 v[kSendRecvSlices];
-#pragma unroll
-        for (int s = 0; s < kSendRecvSlices; ++s) {
-          const int c = (sp * kSendRecvSlices + s) * kSlice + lane;
-          if (c < C) v[s] = x[t * C + c];
-        }
 #pragma unroll
         for (int s = 0; s < kSendRecvSlices; ++s) {
           const int c = (sp * kSendRecvSlices + s) * kSlice + lane;
@@ -1334,9 +1339,12 @@ __global__ __launch_bounds__(kSlice) void combine_kernel(
   }
 }
 
-// Small k (1, 2, 4): one wave covers U slices of a token, so that U * K row
-// loads (16) are in flight per lane; otherwise a k = 2 wave would move only
-// 3 KiB and the launch, not the memory system, would set the pace.
+// Fixed k (1, 2, 4, 8): the token's k rows and weights are loaded first
+// (wave-uniform, scalar), then all U * K row loads go out back to back.  For
+// k < 8 one wave covers U slices of a token, so that 16 row loads are in
+// flight per lane; otherwise a k = 2 wave would move only 3 KiB and the
+// launch, not the memory system, would set the pace.  k = 8 takes one slice
+// (U = 1, 8 loads in flight).
 template <int K, int U>
 __global__ __launch_bounds__(kSlice) void combine_small_k_kernel(
     const u32x4* __restrict__ y, const int32_t* __restrict__ pair_row,
@@ -2071,6 +2079,7 @@ int moe_combine(const void* y, const int32_t* pair_row, const float* topk_w, int
   if (k == 1) return small(combine_small_k_kernel<1, 16>, 16);
   if (k == 2) return small(combine_small_k_kernel<2, 8>, 8);
   if (k == 4) return small(combine_small_k_kernel<4, 4>, 4);
+  if (k == 8) return small(combine_small_k_kernel<8, 1>, 1);
   const int64_t units = T * ncs;
   const unsigned nblocks = unsigned(units < kMaxRowBlocks ? units : kMaxRowBlocks);
   return launch(combine_kernel, dim3(nblocks), dim3(kSlice), 0, s, yv, pair_row, topk_w, T, C, k,
