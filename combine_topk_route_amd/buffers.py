@@ -131,15 +131,15 @@ class MoeBuffers:
             raise ValueError("constructed without fp8=True")
         T = x.shape[0]
         v = self._v(T)
-        s = v.send
-        q, sc = self.buf_q[: T * self.k], self.buf_scale[: T * self.k]
-        _b.moe_route_dispatch_fp8(logits, x, self.k, self.R, n_group=n_group,
-                                  topk_group=topk_group, topk_idx=v.topk_idx, topk_w=v.topk_w,
-                                  buf_q=q, buf_scale=sc, expert_counts=s.expert_counts,
-                                  expert_offsets=s.expert_offsets, pair_row=s.pair_row,
-                                  row_token=s.row_token, rank_offsets=s.rank_offsets,
-                                  workspace=self.route_workspace, stream=stream)
-        return v.topk_idx, v.topk_w, s, q, sc
+        d = self.device_index
+        lp = _b._dev(logits, "logits", torch.float32, 2, device=d)
+        xp = _b._dev(x, "x", torch.bfloat16, 2, device=d)
+        if logits.shape[0] != T or logits.shape[1] != self.E or x.shape[1] != self.H:
+            raise ValueError(f"logits must be [T, {self.E}] and x [T, {self.H}]")
+        _b._check("moe_route_dispatch_fp8", _lib.load().moe_route_dispatch_fp8(
+            lp, xp, T, self.E, self.k, n_group, topk_group, self.H, self.R,
+            *v.route_dispatch_fp8_args, _b._stream(stream, x)))
+        return v.topk_idx, v.topk_w, v.send, v.buf_q, v.buf_scale
 
     def combine(self, y: torch.Tensor, pair_row: torch.Tensor, topk_w: torch.Tensor,
                 stream=None) -> torch.Tensor:
@@ -173,6 +173,13 @@ class _Views:
             s.expert_offsets.data_ptr(), s.pair_row.data_ptr(), s.row_token.data_ptr(),
             s.rank_offsets.data_ptr(), self.buf.data_ptr(), T * b.k,
             b.route_workspace.data_ptr(), b.route_workspace.numel())
+        self.buf_q = self.buf_scale = self.route_dispatch_fp8_args = None
+        if b.buf_q is not None:
+            self.buf_q, self.buf_scale = b.buf_q[: T * b.k], b.buf_scale[: T * b.k]
+            self.route_dispatch_fp8_args = (
+                self.route_dispatch_args[:7]
+                + (self.buf_q.data_ptr(), self.buf_scale.data_ptr())
+                + self.route_dispatch_args[8:])
         self.pair_row_ptr = s.pair_row.data_ptr()
         self.topk_w_ptr = self.topk_w.data_ptr()
         self.out_ptr = self.out.data_ptr()

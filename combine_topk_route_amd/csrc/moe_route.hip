@@ -56,6 +56,10 @@
 //                        its amax is an in-row DPP maximum; the block's waves
 //                        quantise 8 slices into LDS once, then each wave
 //                        streams one destination row's codes and scales.
+//   send_recv_fp8_kernel small batches, as send_recv_kernel with the fp8
+//                        receive: block 0 sends, the other blocks quantise a
+//                        4096-element unit of a token's row into LDS while
+//                        they count its rows, then store it to each of them.
 //   combine_kernel       one wave per (token, 1 KiB column slice): k
 //                        non-temporal 16-byte row loads in flight, fp32 fma
 //                        chain in j order, one bf16 RNE (v_cvt_pk_bf16_f32).
@@ -1102,14 +1106,62 @@ constexpr int64_t kSendRecvMaxPairs = int64_t(kSendWaves) * kWave * kSendItems; 
 constexpr int kSendRecvMaxK = kSendWaves;  // one wave per destination row
 constexpr int kSendRecvSlices = 8;         // 1 KiB slices of a row per copy unit
 
+// The row of pair (t, j) with expert e is the number of pairs with a lower
+// expert (e's offset) plus the number of earlier pairs with expert e (its
+// slot in the stable order).  A block that needs the rows of one token's
+// k <= 8 pairs before the send has written them counts both over topk_idx
+// with ballots, so the counts are wave-uniform and need no reduction inside
+// a wave.  Each wave counts its share of the pairs into part[wid]; after a
+// block barrier, token_rows_finish sums the waves' counts into rows[j]
+// (-1 for an invalid expert, which the send drops).
+__device__ __forceinline__ void token_rows_count(const int32_t* __restrict__ idx, int64_t P,
+                                                 int64_t pt, int k, int wid, int lane,
+                                                 uint32_t (*part)[2 * kSendRecvMaxK]) {
+  int ej[kSendRecvMaxK];
+#pragma unroll
+  for (int j = 0; j < kSendRecvMaxK; ++j) ej[j] = j < k ? idx[pt + j] : -1;
+  uint32_t lt[kSendRecvMaxK], eq[kSendRecvMaxK];
+#pragma unroll
+  for (int j = 0; j < kSendRecvMaxK; ++j) lt[j] = eq[j] = 0u;
+  for (int64_t p0 = int64_t(wid) * kWave; p0 < P; p0 += kSendThreads) {  // wave-uniform bounds
+    const int64_t p = p0 + lane;
+    const bool in = p < P;
+    const int v = in ? idx[p] : -1;
+#pragma unroll
+    for (int j = 0; j < kSendRecvMaxK; ++j) {
+      if (j < k) {
+        lt[j] += __popcll(ballot(in && uint32_t(v) < uint32_t(ej[j])));
+        eq[j] += __popcll(ballot(in && v == ej[j] && p < pt + j));
+      }
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < kSendRecvMaxK; ++j) {
+      part[wid][j] = lt[j];
+      part[wid][kSendRecvMaxK + j] = eq[j];
+    }
+  }
+}
+
+__device__ __forceinline__ void token_rows_finish(const int32_t* __restrict__ idx, int64_t pt,
+                                                  int E, int k,
+                                                  const uint32_t (*part)[2 * kSendRecvMaxK],
+                                                  int32_t* rows) {
+  if (int(threadIdx.x) < k) {
+    const int j = threadIdx.x;
+    const int e = idx[pt + j];
+    uint32_t r = 0u;
+#pragma unroll
+    for (int w = 0; w < kSendWaves; ++w) r += part[w][j] + part[w][kSendRecvMaxK + j];
+    rows[j] = uint32_t(e) < uint32_t(E) ? int32_t(r) : -1;
+  }
+}
+
 // Block 0 runs the single-block send.  Every other block copies up to 8
-// slices of one token's row to the token's k rows, and finds each row
-// itself: the row of pair (t, j) with expert e is the number of pairs with a
-// lower expert (e's offset) plus the number of earlier pairs with expert e
-// (its slot in the stable order).  The block counts both over topk_idx with
-// ballots, so the counts are wave-uniform and need no reduction inside a
-// wave.  The copies never wait for the send, which runs beside them.
-// Wave w copies to destination w (k <= 8).
+// slices of one token's row to the token's k rows, which it finds itself
+// (token_rows_count / token_rows_finish), so the copies never wait for the
+// send, which runs beside them.  Wave w copies to destination w (k <= 8).
 __global__ __launch_bounds__(kSendThreads) void send_recv_kernel(
     const int32_t* __restrict__ idx, int64_t T, int E, int k, int nbits, int L, int R,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -1140,40 +1192,9 @@ __global__ __launch_bounds__(kSendThreads) void send_recv_kernel(
       const int c = (sp * kSendRecvSlices + s) * kSlice + lane;
       v[s] = wid < k && c < C ? x[t * C + c] : u32x4{0u, 0u, 0u, 0u};
     }
-    int ej[kSendRecvMaxK];
-#pragma unroll
-    for (int j = 0; j < kSendRecvMaxK; ++j) ej[j] = j < k ? idx[pt + j] : -1;
-    uint32_t lt[kSendRecvMaxK], eq[kSendRecvMaxK];
-#pragma unroll
-    for (int j = 0; j < kSendRecvMaxK; ++j) lt[j] = eq[j] = 0u;
-    for (int64_t p0 = int64_t(wid) * kWave; p0 < P; p0 += kSendThreads) {  // wave-uniform bounds
-      const int64_t p = p0 + lane;
-      const bool in = p < P;
-      const int v = in ? idx[p] : -1;
-#pragma unroll
-      for (int j = 0; j < kSendRecvMaxK; ++j) {
-        if (j < k) {
-          lt[j] += __popcll(ballot(in && uint32_t(v) < uint32_t(ej[j])));
-          eq[j] += __popcll(ballot(in && v == ej[j] && p < pt + j));
-        }
-      }
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int j = 0; j < kSendRecvMaxK; ++j) {
-        part[wid][j] = lt[j];
-        part[wid][kSendRecvMaxK + j] = eq[j];
-      }
-    }
+    token_rows_count(idx, P, pt, k, wid, lane, part);
     __syncthreads();
-    if (int(threadIdx.x) < k) {
-      const int j = threadIdx.x;
-      const int e = idx[pt + j];
-      uint32_t r = 0u;
-#pragma unroll
-      for (int w = 0; w < kSendWaves; ++w) r += part[w][j] + part[w][kSendRecvMaxK + j];
-      rows[j] = uint32_t(e) < uint32_t(E) ? int32_t(r) : -1;  // an invalid expert: dropped
-    }
+    token_rows_finish(idx, pt, E, k, part, rows);
     __syncthreads();
     if (wid < k) {
       const int32_t r = rows[wid];
@@ -1225,6 +1246,53 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
   return v;
 }
 
+// Wave w of a unit quantises slice w of the unit's 4096 elements (512
+// elements, one 16-byte bf16 chunk per lane: 4 scale blocks of 16 lanes)
+// into the unit's LDS tiles: codes at element offset 512 w, scales at 4 w.
+// Dead chunks (past the row) come in as zeros and are never stored.
+__device__ __forceinline__ void quantise_slice(const u32x4 v, int w, int lane,
+                                               u32x4* __restrict__ q_lds,
+                                               float* __restrict__ s_lds) {
+  float f[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f[2 * q] = __uint_as_float(v[q] << 16);
+    f[2 * q + 1] = __uint_as_float(v[q] & 0xFFFF0000u);
+  }
+  uint32_t amax_bits = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax_bits = max(amax_bits, __float_as_uint(f[i]) & 0x7FFFFFFFu);
+  amax_bits = row16_max_u32(amax_bits);
+  const float amax = __uint_as_float(amax_bits);
+  const float scale = amax > 0.f ? amax / kE4M3Max : 1.0f;
+  uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lo |= e4m3_code(f[i] / scale) << (8 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hi |= e4m3_code(f[4 + i] / scale) << (8 * i);
+  reinterpret_cast<uint2*>(q_lds)[w * kWave + lane] = make_uint2(lo, hi);
+  if ((lane & 15) == 0) s_lds[w * 4 + lane / 16] = scale;
+}
+
+// One wave stores a unit's codes and scales (from the LDS tiles) to
+// destination row r: elements [e0, e0 + 4096) of the row, cut at H.
+__device__ __forceinline__ void store_fp8_unit(const u32x4* __restrict__ q_lds,
+                                               const float* __restrict__ s_lds, int32_t r,
+                                               int e0, int H, int lane,
+                                               uint8_t* __restrict__ buf_q,
+                                               float* __restrict__ buf_s) {
+  const int nbytes = H - e0 < kFp8BlockElems ? H - e0 : kFp8BlockElems;
+  const int nunits = nbytes / 16;
+  const int ns = nbytes / kQuantBlock;
+  u32x4* dq = reinterpret_cast<u32x4*>(buf_q + int64_t(r) * H + e0);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int unit16 = u * kWave + lane;
+    if (unit16 < nunits) __builtin_nontemporal_store(q_lds[unit16], &dq[unit16]);
+  }
+  if (lane < ns) buf_s[int64_t(r) * (H / kQuantBlock) + e0 / kQuantBlock + lane] = s_lds[lane];
+}
+
 __global__ __launch_bounds__(kFp8Waves* kWave) void dispatch_recv_fp8_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ pair_row, int64_t T, int C, int H,
     int k, int nsb, int64_t units, uint8_t* __restrict__ buf_q, float* __restrict__ buf_s,
@@ -1233,53 +1301,67 @@ __global__ __launch_bounds__(kFp8Waves* kWave) void dispatch_recv_fp8_kernel(
   __shared__ float s_lds[kFp8BlockElems / kQuantBlock];  // 32 scales
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = lane_id();
-  const int nscale = H / kQuantBlock;
   for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
     const int64_t t = unit / nsb;
     const int sb = int(unit - t * nsb);
-    // Phase 1: wave w quantises slice sb*8 + w (512 elements, 4 scale blocks).
+    // Phase 1: wave w quantises slice sb*8 + w (whole 16-lane scale blocks
+    // are live or not, since H % 128 == 0).
     const int c = (sb * kFp8Waves + w) * kSlice + lane;  // 16-byte chunk of the bf16 row
-    const bool live = c < C;  // whole 16-lane rows are live or not (H % 128 == 0)
-    const u32x4 v = live ? x[t * C + c] : u32x4{0u, 0u, 0u, 0u};
-    float f[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f[2 * q] = __uint_as_float(v[q] << 16);
-      f[2 * q + 1] = __uint_as_float(v[q] & 0xFFFF0000u);
-    }
-    uint32_t amax_bits = 0u;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax_bits = max(amax_bits, __float_as_uint(f[i]) & 0x7FFFFFFFu);
-    amax_bits = row16_max_u32(amax_bits);
-    const float amax = __uint_as_float(amax_bits);
-    const float scale = amax > 0.f ? amax / kE4M3Max : 1.0f;
-    uint32_t lo = 0u, hi = 0u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= e4m3_code(f[i] / scale) << (8 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= e4m3_code(f[4 + i] / scale) << (8 * i);
-    reinterpret_cast<uint2*>(q_lds)[w * kWave + lane] = make_uint2(lo, hi);
-    if ((lane & 15) == 0) s_lds[w * 4 + lane / 16] = scale;
+    const u32x4 v = c < C ? x[t * C + c] : u32x4{0u, 0u, 0u, 0u};
+    quantise_slice(v, w, lane, q_lds, s_lds);
     __syncthreads();
-    // Phase 2: wave w writes the block's codes and scales to destinations
-    // w, w + 8, ... of token t.
-    const int e0 = sb * kFp8BlockElems;
-    const int nbytes = H - e0 < kFp8BlockElems ? H - e0 : kFp8BlockElems;
-    const int nunits = nbytes / 16;
-    const int ns = nbytes / kQuantBlock;
+    // Phase 2: wave w writes the unit to destinations w, w + 8, ... of token t.
     for (int j = w; j < k; j += kFp8Waves) {
       const int32_t r = pair_row[t * k + j];
-      if (uint64_t(int64_t(r)) < uint64_t(capacity)) {
-        u32x4* dq = reinterpret_cast<u32x4*>(buf_q + int64_t(r) * H + e0);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int unit16 = u * kWave + lane;
-          if (unit16 < nunits) __builtin_nontemporal_store(q_lds[unit16], &dq[unit16]);
-        }
-        if (lane < ns) buf_s[int64_t(r) * nscale + e0 / kQuantBlock + lane] = s_lds[lane];
-      }
+      if (uint64_t(int64_t(r)) < uint64_t(capacity))
+        store_fp8_unit(q_lds, s_lds, r, sb * kFp8BlockElems, H, lane, buf_q, buf_s);
     }
     __syncthreads();  // the LDS tiles are reused by the next unit
+  }
+}
+
+// Send + fp8 recv in one launch for small batches, as send_recv_kernel: block
+// 0 runs the single-block send; every other block quantises one 4096-element
+// unit of a token's row (wave w: slice w) while it counts the token's rows,
+// then wave w stores the unit to destination w (k <= 8).
+static_assert(kFp8Waves == kSendWaves, "one quantising wave per send wave");
+__global__ __launch_bounds__(kSendThreads) void send_recv_fp8_kernel(
+    const int32_t* __restrict__ idx, int64_t T, int E, int k, int nbits, int L, int R,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ pair_row,
+    int32_t* __restrict__ row_token, const u32x4* __restrict__ x, int C, int H, int nsb,
+    int64_t units, uint8_t* __restrict__ buf_q, float* __restrict__ buf_s, int64_t capacity) {
+  extern __shared__ int32_t sm[];
+  const int64_t P = T * k;
+  if (blockIdx.x == 0) {
+    send_rank_block<true, kSendThreads, kSendItems>(0, sm, idx, P, E, k, nbits, P, 1, nullptr,
+                                                    nullptr, L, R, counts, offsets, rank_offsets,
+                                                    pair_row, row_token);
+    return;
+  }
+  __shared__ uint32_t part[kSendWaves][2 * kSendRecvMaxK];
+  __shared__ int32_t rows[kSendRecvMaxK];
+  __shared__ u32x4 q_lds[kFp8BlockElems / 16];
+  __shared__ float s_lds[kFp8BlockElems / kQuantBlock];
+  const int lane = lane_id();
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  for (int64_t unit = blockIdx.x - 1; unit < units; unit += gridDim.x - 1) {
+    const int64_t t = unit / nsb;
+    const int sb = int(unit - t * nsb);
+    const int64_t pt = t * k;
+    const int c = (sb * kFp8Waves + wid) * kSlice + lane;
+    const u32x4 v = c < C ? x[t * C + c] : u32x4{0u, 0u, 0u, 0u};  // in flight while counting
+    token_rows_count(idx, P, pt, k, wid, lane, part);
+    quantise_slice(v, wid, lane, q_lds, s_lds);
+    __syncthreads();
+    token_rows_finish(idx, pt, E, k, part, rows);
+    __syncthreads();
+    if (wid < k) {
+      const int32_t r = rows[wid];
+      if (uint64_t(int64_t(r)) < uint64_t(capacity))
+        store_fp8_unit(q_lds, s_lds, r, sb * kFp8BlockElems, H, lane, buf_q, buf_s);
+    }
+    __syncthreads();  // part, rows and the LDS tiles are reused by the next unit
   }
 }
 
@@ -1727,6 +1809,20 @@ int enqueue_recv_fp8(const void* x, const int32_t* pair_row, int64_t T, int32_t 
                 static_cast<uint8_t*>(buf_q), buf_s, capacity);
 }
 
+int enqueue_send_recv_fp8(const int32_t* topk_idx, const void* x, int64_t T, int32_t E,
+                          int32_t k, int32_t H, int32_t R, int32_t* counts, int32_t* offsets,
+                          int32_t* pair_row, int32_t* row_token, int32_t* rank_offsets,
+                          void* buf_q, float* buf_s, int64_t capacity, hipStream_t st) {
+  const int nsb = (H + kFp8BlockElems - 1) / kFp8BlockElems;
+  const int64_t units = T * nsb;
+  const int64_t copy_blocks = units < kMaxRowBlocks ? units : kMaxRowBlocks;
+  const size_t lds = (size_t(kSendWaves) * E + E + 17) * sizeof(int32_t);
+  return launch(send_recv_fp8_kernel, dim3(unsigned(1 + copy_blocks)), dim3(kSendThreads), lds,
+                st, topk_idx, T, E, k, nbits_for(E), E / R, R, counts, offsets, rank_offsets,
+                pair_row, row_token, static_cast<const u32x4*>(x), H / 8, H, nsb, units,
+                static_cast<uint8_t*>(buf_q), buf_s, capacity);
+}
+
 // Workspace of moe_route_dispatch: a block of arrival counters (word 0: the
 // fused route + send launch; word 1: the rank kernel, whose last block
 // zeroes the histogram matrix), then the send workspace.  All of it holds
@@ -2024,6 +2120,13 @@ int moe_route_dispatch_fp8(const float* logits, const void* x, int64_t T, int32_
   if (workspace == nullptr || workspace_bytes < kArrivalBytes) return MOE_ERR_WORKSPACE;
   if (!aligned(workspace, 4)) return MOE_ERR_ALIGNMENT;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (send_recv_fusable(T, k)) {  // route, then send and fp8 recv in one launch
+    st = enqueue_route(logits, T, E, k, n_group, topk_group, topk_idx, topk_w, s);
+    if (st != MOE_OK) return st;
+    return enqueue_send_recv_fp8(topk_idx, x, T, E, k, H, num_vranks, expert_counts,
+                                 expert_offsets, pair_row, row_token, rank_offsets, buf_q,
+                                 buf_scale, capacity, s);
+  }
   st = enqueue_route_and_send(logits, T, E, k, n_group, topk_group, num_vranks, topk_idx, topk_w,
                               expert_counts, expert_offsets, pair_row, row_token, rank_offsets,
                               workspace, s);
@@ -2052,6 +2155,10 @@ int moe_dispatch_fp8(const int32_t* topk_idx, const void* x, int64_t T, int32_t 
   st = check_fp8_rows(T, H, k, capacity, x, buf_q, buf_scale);
   if (st != MOE_OK || T == 0) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (send_recv_fusable(T, k))
+    return enqueue_send_recv_fp8(topk_idx, x, T, E, k, H, num_vranks, expert_counts,
+                                 expert_offsets, pair_row, row_token, rank_offsets, buf_q,
+                                 buf_scale, capacity, s);
   st = enqueue_send(topk_idx, T, E, k, num_vranks, expert_counts, expert_offsets, pair_row,
                     row_token, rank_offsets, workspace, s);
   if (st != MOE_OK) return st;

@@ -299,6 +299,8 @@ int moe_dispatch_recv_fp8(const void* x, const int32_t* pair_row, int64_t T,
 /*
  * moe_dispatch_fp8 - moe_dispatch_send followed by moe_dispatch_recv_fp8 on
  * one stream; arguments as theirs, all checked before anything is enqueued.
+ * As in moe_dispatch, T*k <= 2048 and k <= 8 run both halves in one launch
+ * (identical results) without the workspace.
  */
 int moe_dispatch_fp8(const int32_t* topk_idx, const void* x, int64_t T,
                      int32_t E, int32_t k, int32_t H, int32_t num_vranks,
@@ -318,7 +320,8 @@ int moe_dispatch_fp8(const int32_t* topk_idx, const void* x, int64_t T,
  * moe_dispatch_recv_fp8 in place of buf; the same workspace rules apply
  * (moe_route_dispatch_workspace_bytes, zeroed once, left zeroed).  All
  * arguments are checked before anything is enqueued.  The outputs equal
- * moe_route_topk_grouped followed by moe_dispatch_fp8.
+ * moe_route_topk_grouped followed by moe_dispatch_fp8, and the launches by
+ * size are moe_route_dispatch's with the fp8 receive in place of the copy.
  * Errors: as moe_route_dispatch and moe_dispatch_recv_fp8.
  */
 int moe_route_dispatch_fp8(const float* logits, const void* x, int64_t T, int32_t E,

@@ -129,3 +129,65 @@ def test_route_dispatch_fp8_matches_the_separate_calls(T, E, k, R, H, G, TG):
     rq, rs = oracle.dispatch_rows_fp8(x, pr, T * k)
     assert np.array_equal(host(q), rq)
     assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32))
+
+
+@pytest.mark.parametrize("T,k,E,R,H,drops", [
+    (1, 1, 1, 1, 128, False), (3, 2, 4, 1, 128, True), (16, 2, 8, 1, 256, False),
+    (128, 8, 256, 32, 7168, False), (128, 8, 256, 32, 7168, True), (256, 8, 256, 32, 4096, True),
+    (300, 6, 40, 8, 8320, True), (2048, 1, 7, 7, 128, False), (682, 3, 1000, 8, 640, True),
+    (683, 3, 1000, 8, 640, True),   # one pair past the one-launch limit
+])
+def test_fp8_dispatch_in_one_launch_matches_send_then_recv(T, k, E, R, H, drops):
+    """moe_dispatch_fp8 sends and quantises in one launch for T*k <= 2048 and
+    k <= 8 (block 0 sends; the other blocks quantise 4096-element units and
+    find their rows from topk_idx).  Against moe_dispatch_send then
+    moe_dispatch_recv_fp8: every send output, code and scale identical, with
+    out-of-range experts (dropped), a repeated expert inside a token, rows
+    cut inside a unit, spare capacity and canary rows; every referenced row
+    holds the oracle's quantisation of its token, and without drops the rows
+    are the oracle's."""
+    import combine_topk_route_amd as m
+
+    print(f"[fp8] dispatch one launch T={T} k={k} E={E} R={R} H={H} drops={drops}", flush=True)
+    rng = np.random.default_rng(T * 11 + k * 5 + E + H)
+    idx = rng.integers(0, E, (T, k)).astype(np.int32)
+    if drops:
+        drop = rng.random((T, k)) < 0.05
+        idx[drop] = rng.choice(np.array([-1, E, E + 5, -(2 ** 31)], np.int32), int(drop.sum()))
+        if T > 2:
+            idx[1, :] = idx[0, 0] if idx[0, 0] >= 0 else 0   # one expert repeated inside a token
+    x = workloads.bf16_from_f32(rng.standard_normal((T, H)).astype(np.float32))
+    cap = T * k + 5
+    out = []
+    for one_call in (True, False):
+        bq = torch.full((cap, H), 0x5A, dtype=torch.uint8, device=DEV)
+        bs = torch.full((cap, H // 128), -2.0, dtype=torch.float32, device=DEV)
+        if one_call:
+            res, _, _ = m.moe_dispatch_fp8(dev_i32(idx), dev_bf16(x), E, R, buf_q=bq, buf_scale=bs,
+                                           capacity=cap)
+        else:
+            res = m.moe_dispatch_send(dev_i32(idx), E, R)
+            m.moe_dispatch_recv_fp8(dev_bf16(x), res.pair_row, buf_q=bq, buf_scale=bs, capacity=cap)
+        torch.cuda.synchronize()
+        out.append((res, host(bq), host(bs)))
+    (a, qa, sa), (b, qb, sb) = out
+    n_valid = int(host(a.expert_offsets)[E])
+    for name in ("expert_counts", "expert_offsets", "pair_row", "rank_offsets"):
+        assert np.array_equal(host(getattr(a, name)), host(getattr(b, name))), name
+    assert np.array_equal(host(a.row_token)[:n_valid], host(b.row_token)[:n_valid])
+    assert np.array_equal(qa, qb)
+    assert np.array_equal(sa.view(np.uint32), sb.view(np.uint32))
+    rq, rs = oracle.quantize_rows(x)
+    pr = host(a.pair_row)
+    t_of, j_of = np.nonzero(pr >= 0)
+    assert len(t_of) == n_valid == int(((idx >= 0) & (idx < E)).sum())
+    rows = pr[t_of, j_of]
+    assert np.array_equal(qa[rows], rq[t_of])
+    assert np.array_equal(sa[rows].view(np.uint32), rs[t_of].view(np.uint32))
+    assert (qa[n_valid:] == 0x5A).all() and (sa[n_valid:] == -2.0).all()
+    if not drops:
+        r_pr, _ = oracle.dispatch_slots(idx, E)
+        assert np.array_equal(pr, r_pr)
+        eq, es = oracle.dispatch_rows_fp8(x, r_pr, cap, np.full((cap, H), 0x5A, np.uint8),
+                                          np.full((cap, H // 128), -2.0, np.float32))
+        assert np.array_equal(qa, eq) and np.array_equal(sa.view(np.uint32), es.view(np.uint32))
