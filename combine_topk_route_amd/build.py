@@ -78,16 +78,17 @@ def build(verbose: bool = False) -> str:
 VARIANT_DIR = os.path.join(ROOT, "_build")
 
 
-def variant_path(slices: int) -> str:
-    return os.path.join(VARIANT_DIR, f"recv_slices_{slices}", "libmoe_route.so")
+def variant_path(name: str) -> str:
+    return os.path.join(VARIANT_DIR, name, "libmoe_route.so")
 
 
-def build_variant(slices: int, verbose: bool = False) -> str:
-    """The library with another slice count per recv wave, for measurement
+def build_variant(name: str, defines: tuple, verbose: bool = False) -> str:
+    """The library built with measurement ``defines`` (another slice count
+    or store form for the recv kernel) under _build/<name>/, for probes.py
     only (never loaded by the package)."""
-    out = variant_path(slices)
+    out = variant_path(name)
     os.makedirs(os.path.dirname(out), exist_ok=True)
-    cmd = command(out + ".tmp", (f"MOE_RECV_SLICES={slices}",))
+    cmd = command(out + ".tmp", defines)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

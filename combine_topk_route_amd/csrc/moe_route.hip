@@ -1035,6 +1035,31 @@ constexpr int64_t kMaxRowBlocks = int64_t(1) << 21;  // beyond this, blocks loop
 constexpr int kRecvSlices = MOE_RECV_SLICES;
 static_assert(kRecvSlices >= 1 && kRecvSlices <= 8, "slices per recv wave");
 
+// The recv kernel's stores: global stores with the non-temporal hint.  A
+// buffer written once and read by a later kernel gains nothing from being
+// kept in the L2 or the Infinity Cache, and write-back stores there cost
+// more than they save when x is cache-resident.  For measurement,
+// MOE_RECV_STORE = 0..31 builds the kernel with buffer stores carrying that
+// cache-policy word instead (sc0 = 1, nt = 2, sc1 = 16); such a build takes
+// buffers of at most 4 GiB.
+#ifndef MOE_RECV_STORE
+#define MOE_RECV_STORE -1
+#endif
+constexpr int kRecvStore = MOE_RECV_STORE;
+static_assert(kRecvStore >= -1 && kRecvStore <= 31, "recv store form");
+
+// Store v as 16-byte chunk i of buf (nbytes: the buffer's size in bytes,
+// used only by the measurement forms).
+__device__ __forceinline__ void recv_store(const u32x4 v, u32x4* __restrict__ buf, int64_t i,
+                                           uint32_t nbytes) {
+  if constexpr (kRecvStore < 0) {
+    __builtin_nontemporal_store(v, &buf[i]);
+  } else {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(buf, 0, nbytes, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, uint32_t(i) * 16u, 0, kRecvStore);
+  }
+}
+
 struct RecvPlan {
   int groups;  // waves per block; wave g writes destinations g*per .. g*per+per-1
   int per;
@@ -1062,6 +1087,7 @@ __global__ __launch_bounds__(kMaxRowThreads) void dispatch_recv_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ pair_row, int64_t T, int C, int k,
     int per, int nsb, int64_t units, u32x4* __restrict__ buf, int64_t capacity) {
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x / kSlice);
+  const uint32_t nbytes = kRecvStore < 0 ? 0u : uint32_t(capacity * C * 16);
   for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
     const int64_t t = unit / nsb;
     const int c0 = int(unit - t * nsb) * (U * kSlice) + lane_id();
@@ -1091,7 +1117,7 @@ __global__ __launch_bounds__(kMaxRowThreads) void dispatch_recv_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int c = c0 + u * kSlice;
-          if (c < C) __builtin_nontemporal_store(v[u], &buf[int64_t(r[jj]) * C + c]);
+          if (c < C) recv_store(v[u], buf, int64_t(r[jj]) * C + c, nbytes);
         }
       }
     }
@@ -1760,6 +1786,8 @@ int enqueue_recv(const void* x, const int32_t* pair_row, int64_t T, int32_t H, i
                  void* buf, int64_t capacity, hipStream_t st) {
   const int C = H / 8;
   const RecvPlan p = plan_recv(T, C, k);
+  if (kRecvStore >= 0 && uint64_t(capacity) * uint64_t(C) * 16u > 0xFFFFFFFFull)
+    return MOE_ERR_INVALID_ARG;  // a measurement build: buffer stores address 4 GiB
   return launch(dispatch_recv_kernel<kRecvSlices>, dim3(p.nblocks), dim3(p.groups * kSlice), 0,
                 st, static_cast<const u32x4*>(x), pair_row, T, C, k, p.per, p.nsb, p.units,
                 static_cast<u32x4*>(buf), capacity);

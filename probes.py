@@ -5,6 +5,7 @@
     python probes.py write_fronts [--config dsv3_prefill] [--launches 3]
     python probes.py cu_scaling [--config dsv3_prefill] [--reps 20]
     python probes.py overlap_masked [--config dsv3_prefill] [--reps 20]
+    python probes.py store_policy [--config dsv3_prefill] [--reps 20]
 
 Each prints one JSON line (write_fronts prints it after its launches, which a
 rocprofv3 --pmc run records per dispatch).
@@ -25,6 +26,9 @@ rocprofv3 --pmc run records per dispatch).
 * cu_scaling: recv on streams restricted to n of the chip's CUs
   (hipExtStreamCreateWithCUMask), n = 32 .. all, CUs taken evenly over the
   chip or the first n.
+* store_policy: the recv kernel with its stores as buffer stores under each
+  cache policy (plain write-back, sc0, nt, sc1, nt sc1; MOE_RECV_STORE)
+  against the library's global non-temporal stores, warm and cold.
 * overlap_masked: dispatch beside the stand-in shared-expert GEMM, back to
   back, on two unmasked streams, and with the CUs split between two masked
   streams.
@@ -75,22 +79,38 @@ def _setup(name, seed=0, zipf_s="config"):
     return d
 
 
-def _recv_variant(slices):
-    """C entry moe_dispatch_recv of the library built with `slices`."""
+def _recv_variant(name=None, defines=()):
+    """C entry moe_dispatch_recv of the library (name None) or of the
+    measurement build `name` with `defines`."""
     import combine_topk_route_amd as m
     from combine_topk_route_amd import build as b
 
-    if slices == LIB_SLICES:
-        lib = m._lib.load()
-    else:
-        path = b.variant_path(slices)
-        if not os.path.exists(path):
-            b.build_variant(slices)
-        lib = ctypes.CDLL(path)
-        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
-        lib.moe_dispatch_recv.argtypes = [vp, vp, i64, i32, i32, vp, i64, vp]
-        lib.moe_dispatch_recv.restype = ctypes.c_int
+    if name is None:
+        return m._lib.load().moe_dispatch_recv
+    path = b.variant_path(name)
+    if not os.path.exists(path):
+        b.build_variant(name, defines)
+    lib = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.moe_dispatch_recv.argtypes = [vp, vp, i64, i32, i32, vp, i64, vp]
+    lib.moe_dispatch_recv.restype = ctypes.c_int
     return lib.moe_dispatch_recv
+
+
+def _slice_variant(slices):
+    if slices == LIB_SLICES:
+        return None, ()
+    return f"recv_slices_{slices}", (f"MOE_RECV_SLICES={slices}",)
+
+
+# Store forms of the recv kernel: cache-policy words of a buffer store
+# (sc0 = 1, nt = 2, sc1 = 16); the library uses a global non-temporal store.
+STORE_FORMS = {"plain": 0, "sc0": 1, "nt": 2, "sc1": 16, "nt sc1": 18}
+
+
+def _store_variant(form):
+    cpol = STORE_FORMS[form]
+    return f"recv_store_{cpol}", (f"MOE_RECV_STORE={cpol}",)
 
 
 class _Timer:
@@ -129,7 +149,11 @@ def _recv_bytes(cfg):
     return 2 * cfg.T * cfg.H + 2 * cfg.P * cfg.H + 4 * cfg.P
 
 
-def _slices_rows(d, timer, slices_list):
+def _variant_rows(d, timer, variants):
+    """variants: (label, name, defines) -> warm/cold rows, each buffer
+    checked bit for bit against the library's."""
+    import torch
+
     import combine_topk_route_amd as m
 
     cfg = d["cfg"]
@@ -138,26 +162,31 @@ def _slices_rows(d, timer, slices_list):
     comb = lambda: m.moe_combine(d["y"], d["send"].pair_row, d["w"], out=d["out"],
                                  stream=timer.stream)
     rows = []
-    for u in slices_list:
-        fn_c = _recv_variant(u)
+    for label, name, defines in variants:
+        fn_c = _recv_variant(name, defines)
         call = lambda: fn_c(d["x"].data_ptr(), d["send"].pair_row.data_ptr(), cfg.T, cfg.H,
                             cfg.k, d["buf"].data_ptr(), cfg.P, st)
         d["buf"].zero_()
         rc = call()
-        import torch
-
         torch.cuda.synchronize()
         same = rc == 0 and torch.equal(d["buf"].view(torch.int16), ref.view(torch.int16))
         warm = timer.median_us(call, comb)
         cold = timer.median_us(call, timer.cold)
         nb = _recv_bytes(cfg)
-        rows.append({"slices": u, "library": u == LIB_SLICES, "bit_exact": bool(same),
+        rows.append({"variant": label, "library": name is None, "bit_exact": bool(same),
                      "warm_us": round(warm, 1), "cold_us": round(cold, 1),
                      "warm_frac": round(nb / warm / 1e3 / 8000.0, 4),
                      "cold_frac": round(nb / cold / 1e3 / 8000.0, 4)})
-        print(f"[probe] {cfg.name} slices {u}: warm {warm:.1f} us cold {cold:.1f} us",
+        print(f"[probe] {cfg.name} {label}: warm {warm:.1f} us cold {cold:.1f} us",
               file=sys.stderr, flush=True)
     del ref
+    return rows
+
+
+def _slices_rows(d, timer, slices_list):
+    rows = _variant_rows(d, timer, [(u, *_slice_variant(u)) for u in slices_list])
+    for r in rows:
+        r["slices"] = r.pop("variant")
     return rows
 
 
@@ -167,6 +196,16 @@ def probe_recv_slices(args):
     rows = _slices_rows(d, timer, (1, 2, 4))
     return {"probe": "recv_slices", "workload": args.config, "n_eff": round(d["n_eff"], 1),
             "active_experts": d["active_experts"], "reps": args.reps, "rows": rows}
+
+
+def probe_store_policy(args):
+    timer = _Timer(args.reps)
+    d = _setup(args.config)
+    variants = [("global nt (library)", None, ())]
+    variants += [(form, *_store_variant(form)) for form in STORE_FORMS]
+    rows = _variant_rows(d, timer, variants)
+    return {"probe": "store_policy", "workload": args.config, "n_eff": round(d["n_eff"], 1),
+            "reps": args.reps, "rows": rows}
 
 
 def probe_skew(args):
@@ -362,7 +401,7 @@ def probe_overlap_masked(args):
 
 PROBES = {"recv_slices": probe_recv_slices, "skew": probe_skew,
           "write_fronts": probe_write_fronts, "cu_scaling": probe_cu_scaling,
-          "overlap_masked": probe_overlap_masked}
+          "overlap_masked": probe_overlap_masked, "store_policy": probe_store_policy}
 
 
 def main() -> int:
@@ -375,8 +414,9 @@ def main() -> int:
     if args.probe == "build":  # the variant libraries, on a machine with hipcc
         from combine_topk_route_amd import build as b
 
-        for u in (1, 4):
-            print(b.build_variant(u, verbose=True), flush=True)
+        for name, defines in [_slice_variant(1), _slice_variant(4)] + [
+                _store_variant(f) for f in STORE_FORMS]:
+            print(b.build_variant(name, defines, verbose=True), flush=True)
         return 0
     import torch
 
