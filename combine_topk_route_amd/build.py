@@ -24,14 +24,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmoe_route.so)")
 
 
-def command(out: str = LIB, defines: tuple = ()) -> list[str]:
+def command(out: str = LIB, defines: tuple = (), src: str = SRC) -> list[str]:
     """hipcc command line; ``defines`` (e.g. ``("MOE_RECV_SLICES=1",)``) build
-    the measurement variants that probes.py compares against the library."""
+    the measurement variants that probes.py compares against the library,
+    and ``src`` its own measurement kernels."""
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # keep the compiler from forming packed fp32 VALU ops
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wall", f"-I{INCLUDE}", *[f"-D{d}" for d in defines], "-o", out, SRC,
+        "-Wall", f"-I{INCLUDE}", *[f"-D{d}" for d in defines], "-o", out, src,
     ]
 
 
@@ -78,17 +79,18 @@ def build(verbose: bool = False) -> str:
 VARIANT_DIR = os.path.join(ROOT, "_build")
 
 
-def variant_path(name: str) -> str:
-    return os.path.join(VARIANT_DIR, name, "libmoe_route.so")
+def variant_path(name: str, lib: str = "libmoe_route.so") -> str:
+    return os.path.join(VARIANT_DIR, name, lib)
 
 
-def build_variant(name: str, defines: tuple, verbose: bool = False) -> str:
+def build_variant(name: str, defines: tuple, verbose: bool = False, src: str = SRC,
+                  lib: str = "libmoe_route.so") -> str:
     """The library built with measurement ``defines`` (another slice count
-    or store form for the recv kernel) under _build/<name>/, for probes.py
-    only (never loaded by the package)."""
-    out = variant_path(name)
+    or store form for the recv kernel), or another measurement source, as
+    _build/<name>/<lib>, for probes.py only (never loaded by the package)."""
+    out = variant_path(name, lib)
     os.makedirs(os.path.dirname(out), exist_ok=True)
-    cmd = command(out + ".tmp", defines)
+    cmd = command(out + ".tmp", defines, src)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -6,6 +6,7 @@
     python probes.py cu_scaling [--config dsv3_prefill] [--reps 20]
     python probes.py overlap_masked [--config dsv3_prefill] [--reps 20]
     python probes.py store_policy [--config dsv3_prefill] [--reps 20]
+    python probes.py hbm_ceiling [--reps 20]
 
 Each prints one JSON line (write_fronts prints it after its launches, which a
 rocprofv3 --pmc run records per dispatch).
@@ -29,6 +30,10 @@ rocprofv3 --pmc run records per dispatch).
 * store_policy: the recv kernel with its stores as buffer stores under each
   cache policy (plain write-back, sc0, nt, sc1, nt sc1; MOE_RECV_STORE)
   against the library's global non-temporal stores, warm and cold.
+* hbm_ceiling: the chip's practical HBM rates for plain streaming kernels
+  (read, write and copy over 4 GiB at several grid sizes), and chunk writes
+  of 1-16 KiB in order against a random order: the ceilings the row kernels
+  are held against besides the 8 TB/s peak.
 * overlap_masked: dispatch beside the stand-in shared-expert GEMM, back to
   back, on two unmasked streams, and with the CUs split between two masked
   streams.
@@ -206,6 +211,154 @@ def probe_store_policy(args):
     rows = _variant_rows(d, timer, variants)
     return {"probe": "store_policy", "workload": args.config, "n_eff": round(d["n_eff"], 1),
             "reps": args.reps, "rows": rows}
+
+
+# Streaming kernels for the practical HBM ceilings (16-byte accesses, 256
+# threads per block, grid-stride).  chunk_write: wave w of the grid writes
+# chunk order[w] of the buffer (kib KiB, one 1 KiB store per lane each), so
+# the host sets the write pattern: chunks in order, or a random permutation.
+CEILING_SRC = r"""
+#include <hip/hip_runtime.h>
+#include <cstdint>
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__global__ __launch_bounds__(256) void stream_write(u32x4* __restrict__ d, int64_t n) {
+  const u32x4 val = {1u, 2u, 3u, 4u};
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+    if (NT) __builtin_nontemporal_store(val, &d[i]); else d[i] = val;
+  }
+}
+
+template <bool NT>
+__global__ __launch_bounds__(256) void stream_read(const u32x4* __restrict__ s, int64_t n,
+                                                   uint32_t* __restrict__ sink) {
+  uint32_t acc = 0u;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+    const u32x4 v = NT ? __builtin_nontemporal_load(&s[i]) : s[i];
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;  // keeps the loads; the data never matches
+}
+
+template <bool NT>
+__global__ __launch_bounds__(256) void stream_copy(const u32x4* __restrict__ s,
+                                                   u32x4* __restrict__ d, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+    const u32x4 v = s[i];
+    if (NT) __builtin_nontemporal_store(v, &d[i]); else d[i] = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void chunk_write(u32x4* __restrict__ d,
+                                                   const int32_t* __restrict__ order,
+                                                   int64_t nchunks, int kib) {
+  const int64_t w = int64_t(blockIdx.x) * 4 + threadIdx.x / 64;
+  if (w >= nchunks) return;
+  const int64_t c = order[w];
+  const u32x4 val = {5u, 6u, 7u, 8u};
+  const int lane = threadIdx.x % 64;
+  for (int s = 0; s < kib; ++s) __builtin_nontemporal_store(val, &d[(c * kib + s) * 64 + lane]);
+}
+
+extern "C" int ceiling_launch(int op, void* a, void* b, int64_t n16, int64_t blocks,
+                              void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 g{static_cast<unsigned>(blocks)}, t{256u};
+  switch (op) {
+    case 0: hipLaunchKernelGGL(stream_write<true>, g, t, 0, st, (u32x4*)a, n16); break;
+    case 1: hipLaunchKernelGGL(stream_write<false>, g, t, 0, st, (u32x4*)a, n16); break;
+    case 2: hipLaunchKernelGGL(stream_read<true>, g, t, 0, st, (const u32x4*)a, n16, (uint32_t*)b); break;
+    case 3: hipLaunchKernelGGL(stream_read<false>, g, t, 0, st, (const u32x4*)a, n16, (uint32_t*)b); break;
+    case 4: hipLaunchKernelGGL(stream_copy<true>, g, t, 0, st, (const u32x4*)a, (u32x4*)b, n16); break;
+    case 5: hipLaunchKernelGGL(stream_copy<false>, g, t, 0, st, (const u32x4*)a, (u32x4*)b, n16); break;
+    case 6: {  // blocks: KiB per chunk
+      const int64_t nchunks = n16 / (64 * blocks);
+      hipLaunchKernelGGL(chunk_write, dim3(unsigned((nchunks + 3) / 4)), t, 0, st, (u32x4*)a,
+                         (const int32_t*)b, nchunks, int(blocks));
+      break;
+    }
+    default: return 2;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+"""
+
+CEILING_OPS = {0: "write, nt stores", 1: "write, plain stores", 2: "read, nt loads",
+               3: "read, plain loads", 4: "copy, nt stores", 5: "copy, plain stores"}
+
+
+def _ceiling_lib():
+    from combine_topk_route_amd import build as b
+
+    path = b.variant_path("hbm_ceiling", "libhbm_ceiling.so")
+    if not os.path.exists(path):
+        src = os.path.join(os.path.dirname(path), "hbm_ceiling.hip")
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+        with open(src, "w") as f:
+            f.write(CEILING_SRC)
+        b.build_variant("hbm_ceiling", (), src=src, lib="libhbm_ceiling.so")
+    lib = ctypes.CDLL(path)
+    lib.ceiling_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    lib.ceiling_launch.restype = ctypes.c_int
+    return lib
+
+
+def probe_hbm_ceiling(args):
+    """Back-to-back launches over 4 GiB buffers (16 times the Infinity
+    Cache): read, write and copy at several grid sizes, and chunk writes of
+    1-16 KiB in order against a random permutation of the chunks."""
+    import numpy as np
+    import torch
+
+    lib = _ceiling_lib()
+    st = torch.cuda.current_stream()
+    size = 4 << 30
+    n16 = size // 16
+    a = torch.empty(size, dtype=torch.uint8, device="cuda")
+    b = torch.empty(size, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1 << 20, dtype=torch.int32, device="cuda")
+
+    def timed(op, x, y, blocks):
+        for _ in range(3):
+            assert lib.ceiling_launch(op, x, y, n16, blocks, st.cuda_stream) == 0
+        ev = []
+        for _ in range(args.reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            assert lib.ceiling_launch(op, x, y, n16, blocks, st.cuda_stream) == 0
+            e1.record(st)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) * 1000.0 for e0, e1 in ev]))
+
+    assert lib.ceiling_launch(0, a.data_ptr(), None, n16, 8192, st.cuda_stream) == 0
+    rows = []
+    for blocks in (2048, 8192, 32768, 131072):
+        for op, name in CEILING_OPS.items():
+            y = sink.data_ptr() if op in (2, 3) else b.data_ptr()
+            us = timed(op, a.data_ptr(), y, blocks)
+            nbytes = size * (2 if op in (4, 5) else 1)
+            rows.append({"op": name, "blocks": blocks, "us": round(us, 1),
+                         "TBps": round(nbytes / us / 1e6, 3)})
+            print(f"[probe] {name} {blocks} blocks: {nbytes / us / 1e6:.2f} TB/s", file=sys.stderr,
+                  flush=True)
+    rng = np.random.default_rng(0)
+    for kib in (1, 2, 4, 8, 14, 16):
+        nchunks = size // (1024 * kib)
+        used = nchunks * 1024 * kib
+        for order_name, order in (("in order", np.arange(nchunks, dtype=np.int32)),
+                                  ("random order", rng.permutation(nchunks).astype(np.int32))):
+            o = torch.from_numpy(order).cuda()
+            us = timed(6, a.data_ptr(), o.data_ptr(), kib)
+            rows.append({"op": f"{kib} KiB chunk writes, {order_name}",
+                         "blocks": (nchunks + 3) // 4, "us": round(us, 1),
+                         "TBps": round(used / us / 1e6, 3)})
+            print(f"[probe] {kib} KiB chunks {order_name}: {used / us / 1e6:.2f} TB/s",
+                  file=sys.stderr, flush=True)
+            del o
+    return {"probe": "hbm_ceiling", "bytes": size, "reps": args.reps, "rows": rows}
 
 
 def probe_skew(args):
@@ -401,7 +554,8 @@ def probe_overlap_masked(args):
 
 PROBES = {"recv_slices": probe_recv_slices, "skew": probe_skew,
           "write_fronts": probe_write_fronts, "cu_scaling": probe_cu_scaling,
-          "overlap_masked": probe_overlap_masked, "store_policy": probe_store_policy}
+          "overlap_masked": probe_overlap_masked, "store_policy": probe_store_policy,
+          "hbm_ceiling": probe_hbm_ceiling}
 
 
 def main() -> int:
@@ -417,6 +571,8 @@ def main() -> int:
         for name, defines in [_slice_variant(1), _slice_variant(4)] + [
                 _store_variant(f) for f in STORE_FORMS]:
             print(b.build_variant(name, defines, verbose=True), flush=True)
+        _ceiling_lib()
+        print(b.variant_path("hbm_ceiling", "libhbm_ceiling.so"), flush=True)
         return 0
     import torch
 
