@@ -7,6 +7,7 @@
     python probes.py overlap_masked [--config dsv3_prefill] [--reps 20]
     python probes.py store_policy [--config dsv3_prefill] [--reps 20]
     python probes.py hbm_ceiling [--reps 20]
+    python probes.py combine_store [--reps 20]
 
 Each prints one JSON line (write_fronts prints it after its launches, which a
 rocprofv3 --pmc run records per dispatch).
@@ -30,10 +31,13 @@ rocprofv3 --pmc run records per dispatch).
 * store_policy: the recv kernel with its stores as buffer stores under each
   cache policy (plain write-back, sc0, nt, sc1, nt sc1; MOE_RECV_STORE)
   against the library's global non-temporal stores, warm and cold.
+* combine_store: moe_combine as built (sc1 output stores above 256 MiB of
+  combine bytes, write-back below) against builds that force either form
+  (MOE_COMBINE_SC1_MIN_BYTES), on every workload, warm and cold.
 * hbm_ceiling: the chip's practical HBM rates for plain streaming kernels
   (read, write and copy over 4 GiB at several grid sizes), and chunk writes
-  of 1-16 KiB in order against a random order: the ceilings the row kernels
-  are held against besides the 8 TB/s peak.
+  and reads of 1-16 KiB in order against a random order: the ceilings the
+  row kernels are held against besides the 8 TB/s peak.
 * overlap_masked: dispatch beside the stand-in shared-expert GEMM, back to
   back, on two unmasked streams, and with the CUs split between two masked
   streams.
@@ -203,6 +207,70 @@ def probe_recv_slices(args):
             "active_experts": d["active_experts"], "reps": args.reps, "rows": rows}
 
 
+# Combine's output store: the library picks sc1 above 256 MiB of combine
+# bytes and write-back below; these builds force one form at every size.
+COMBINE_STORE_FORMS = {"sc1 at every size": "0", "write-back at every size": "INT64_MAX"}
+
+
+def _combine_variant(form):
+    tag = "sc1" if COMBINE_STORE_FORMS[form] == "0" else "wb"
+    return f"combine_store_{tag}", (f"MOE_COMBINE_SC1_MIN_BYTES={COMBINE_STORE_FORMS[form]}",)
+
+
+def probe_combine_store(args):
+    """moe_combine of the library against the builds that force sc1 or
+    write-back output stores, on every workload: warm (right after a recv of
+    the same workload, as in a step) and cold (after the read sweep)."""
+    import torch
+
+    import combine_topk_route_amd as m
+    import workloads
+    from combine_topk_route_amd import _lib
+
+    fns = {"library (by size)": m._lib.load().moe_combine}
+    for form in COMBINE_STORE_FORMS:
+        name, defines = _combine_variant(form)
+        from combine_topk_route_amd import build as b
+
+        path = b.variant_path(name)
+        if not os.path.exists(path):
+            b.build_variant(name, defines)
+        lib = ctypes.CDLL(path)
+        res, argt = _lib.SIGNATURES["moe_combine"]
+        lib.moe_combine.restype, lib.moe_combine.argtypes = res, argt
+        fns[form] = lib.moe_combine
+    timer = _Timer(args.reps)
+    out = []
+    for name in workloads.CONFIGS:
+        d = _setup(name)
+        cfg = d["cfg"]
+        st = timer.stream.cuda_stream
+        s = d["send"]
+        ref = m.moe_combine(d["y"], s.pair_row, d["w"])
+        recv = lambda: m.moe_dispatch_recv(d["x"], s.pair_row, buf=d["buf"], stream=timer.stream)
+        nb = 2 * cfg.P * cfg.H + 8 * cfg.P + 2 * cfg.T * cfg.H
+        rows = []
+        for label, fn in fns.items():
+            call = lambda: fn(d["y"].data_ptr(), s.pair_row.data_ptr(), d["w"].data_ptr(), cfg.T,
+                              cfg.H, cfg.k, cfg.P, d["out"].data_ptr(), st)
+            d["out"].zero_()
+            rc = call()
+            torch.cuda.synchronize()
+            same = rc == 0 and torch.equal(d["out"].view(torch.int16), ref.view(torch.int16))
+            warm = timer.median_us(call, recv)
+            cold = timer.median_us(call, timer.cold)
+            rows.append({"variant": label, "bit_exact": bool(same), "warm_us": round(warm, 2),
+                         "cold_us": round(cold, 2),
+                         "warm_frac": round(nb / warm / 1e3 / 8000.0, 4),
+                         "cold_frac": round(nb / cold / 1e3 / 8000.0, 4)})
+            print(f"[probe] {name} {label}: warm {warm:.2f} us cold {cold:.2f} us",
+                  file=sys.stderr, flush=True)
+        out.append({"workload": name, "bytes": nb, "rows": rows})
+        del d, ref
+        torch.cuda.empty_cache()
+    return {"probe": "combine_store", "reps": args.reps, "workloads": out}
+
+
 def probe_store_policy(args):
     timer = _Timer(args.reps)
     d = _setup(args.config)
@@ -214,9 +282,10 @@ def probe_store_policy(args):
 
 
 # Streaming kernels for the practical HBM ceilings (16-byte accesses, 256
-# threads per block, grid-stride).  chunk_write: wave w of the grid writes
-# chunk order[w] of the buffer (kib KiB, one 1 KiB store per lane each), so
-# the host sets the write pattern: chunks in order, or a random permutation.
+# threads per block, grid-stride).  chunk_write / chunk_read: wave w of the
+# grid writes / reads chunk order[w] of the buffer (kib KiB, one 16-byte
+# access per lane per KiB), so the host sets the pattern: chunks in order,
+# or a random permutation.
 CEILING_SRC = r"""
 #include <hip/hip_runtime.h>
 #include <cstdint>
@@ -261,6 +330,22 @@ __global__ __launch_bounds__(256) void chunk_write(u32x4* __restrict__ d,
   for (int s = 0; s < kib; ++s) __builtin_nontemporal_store(val, &d[(c * kib + s) * 64 + lane]);
 }
 
+__global__ __launch_bounds__(256) void chunk_read(const u32x4* __restrict__ s,
+                                                  const int32_t* __restrict__ order,
+                                                  int64_t nchunks, int kib,
+                                                  uint32_t* __restrict__ sink) {
+  const int64_t w = int64_t(blockIdx.x) * 4 + threadIdx.x / 64;
+  if (w >= nchunks) return;
+  const int64_t c = order[w];
+  const int lane = threadIdx.x % 64;
+  uint32_t acc = 0u;
+  for (int q = 0; q < kib; ++q) {
+    const u32x4 v = __builtin_nontemporal_load(&s[(c * kib + q) * 64 + lane]);
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  if (acc == 0x9E3779B9u) sink[w & 1023] = acc;  // keeps the loads; the data never matches
+}
+
 extern "C" int ceiling_launch(int op, void* a, void* b, int64_t n16, int64_t blocks,
                               void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -276,6 +361,13 @@ extern "C" int ceiling_launch(int op, void* a, void* b, int64_t n16, int64_t blo
       const int64_t nchunks = n16 / (64 * blocks);
       hipLaunchKernelGGL(chunk_write, dim3(unsigned((nchunks + 3) / 4)), t, 0, st, (u32x4*)a,
                          (const int32_t*)b, nchunks, int(blocks));
+      break;
+    }
+    case 7: {  // chunk reads; b: [order | sink], blocks: KiB per chunk
+      const int64_t nchunks = n16 / (64 * blocks);
+      hipLaunchKernelGGL(chunk_read, dim3(unsigned((nchunks + 3) / 4)), t, 0, st,
+                         (const u32x4*)a, (const int32_t*)b, nchunks, int(blocks),
+                         (uint32_t*)b + nchunks);
       break;
     }
     default: return 2;
@@ -307,8 +399,8 @@ def _ceiling_lib():
 
 def probe_hbm_ceiling(args):
     """Back-to-back launches over 4 GiB buffers (16 times the Infinity
-    Cache): read, write and copy at several grid sizes, and chunk writes of
-    1-16 KiB in order against a random permutation of the chunks."""
+    Cache): read, write and copy at several grid sizes, and chunk writes and
+    reads of 1-16 KiB in order against a random permutation of the chunks."""
     import numpy as np
     import torch
 
@@ -350,13 +442,16 @@ def probe_hbm_ceiling(args):
         used = nchunks * 1024 * kib
         for order_name, order in (("in order", np.arange(nchunks, dtype=np.int32)),
                                   ("random order", rng.permutation(nchunks).astype(np.int32))):
-            o = torch.from_numpy(order).cuda()
-            us = timed(6, a.data_ptr(), o.data_ptr(), kib)
-            rows.append({"op": f"{kib} KiB chunk writes, {order_name}",
-                         "blocks": (nchunks + 3) // 4, "us": round(us, 1),
-                         "TBps": round(used / us / 1e6, 3)})
-            print(f"[probe] {kib} KiB chunks {order_name}: {used / us / 1e6:.2f} TB/s",
-                  file=sys.stderr, flush=True)
+            # the order, then 1024 words of sink for the reads
+            o = torch.zeros(nchunks + 1024, dtype=torch.int32, device="cuda")
+            o[:nchunks] = torch.from_numpy(order).cuda()
+            for op, what in ((6, "writes"), (7, "reads")):
+                us = timed(op, a.data_ptr(), o.data_ptr(), kib)
+                rows.append({"op": f"{kib} KiB chunk {what}, {order_name}",
+                             "blocks": (nchunks + 3) // 4, "us": round(us, 1),
+                             "TBps": round(used / us / 1e6, 3)})
+                print(f"[probe] {kib} KiB chunk {what} {order_name}: {used / us / 1e6:.2f} TB/s",
+                      file=sys.stderr, flush=True)
             del o
     return {"probe": "hbm_ceiling", "bytes": size, "reps": args.reps, "rows": rows}
 
@@ -555,7 +650,7 @@ def probe_overlap_masked(args):
 PROBES = {"recv_slices": probe_recv_slices, "skew": probe_skew,
           "write_fronts": probe_write_fronts, "cu_scaling": probe_cu_scaling,
           "overlap_masked": probe_overlap_masked, "store_policy": probe_store_policy,
-          "hbm_ceiling": probe_hbm_ceiling}
+          "hbm_ceiling": probe_hbm_ceiling, "combine_store": probe_combine_store}
 
 
 def main() -> int:
@@ -569,7 +664,8 @@ def main() -> int:
         from combine_topk_route_amd import build as b
 
         for name, defines in [_slice_variant(1), _slice_variant(4)] + [
-                _store_variant(f) for f in STORE_FORMS]:
+                _store_variant(f) for f in STORE_FORMS] + [
+                _combine_variant(f) for f in COMBINE_STORE_FORMS]:
             print(b.build_variant(name, defines, verbose=True), flush=True)
         _ceiling_lib()
         print(b.variant_path("hbm_ceiling", "libhbm_ceiling.so"), flush=True)
