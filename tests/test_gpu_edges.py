@@ -436,3 +436,71 @@ def test_dirty_route_dispatch_workspace_stays_in_bounds():
     assert_step_matches_oracle(lg, xb, k, E, R, idx, w,
                                (counts, offsets, pair_row, row_token[:P], rank_off), buf)
     assert int(ws.count_nonzero().item()) == 0
+
+
+SC1_MIN_BYTES = 256 << 20   # combine bytes above which output rows take the sc1 stores
+
+
+@pytest.mark.parametrize("T,H,k", [
+    (2675, 7168, 6), (2674, 7168, 6),     # combine_kernel: just above / below the threshold
+    (10923, 4096, 2), (10922, 4096, 2),   # the fixed-k kernel at k = 2
+    (6554, 4096, 4), (6553, 4096, 4),     # and at k = 4
+])
+def test_combine_on_both_sides_of_the_store_threshold(T, H, k):
+    """moe_combine stores its output rows with the sc1 cache policy when it
+    moves more than 256 MiB (2TkH + 2TH bytes) and with write-back stores
+    below; both forms of every kernel shape against the oracle on every
+    token, with spare capacity."""
+    m = _m()
+    nbytes = 2 * T * H * (k + 1)
+    above = nbytes > SC1_MIN_BYTES
+    print(f"[edges] combine T={T} H={H} k={k} bytes={nbytes} sc1={above}", flush=True)
+    rng = np.random.default_rng(T * 31 + k)
+    P = T * k
+    cap = P + 5
+    pr = rng.permutation(cap)[:P].reshape(T, k).astype(np.int32)
+    y = _rand_bf16((cap, H), T + k)
+    w = rng.random((T, k)).astype(np.float32)
+    out = host_bf16(m.moe_combine(dev_bf16(y), dev_i32(pr), dev_f32(w)))
+    torch.cuda.synchronize()
+    for t0 in range(0, T, 1024):
+        t1 = min(T, t0 + 1024)
+        ref = oracle.combine_tokens(y, pr, w, np.arange(t0, t1))
+        assert np.array_equal(out[t0:t1], ref), f"tokens [{t0}, {t1}) differ"
+
+
+def _combine_skipping(y, pr, w, cap):
+    """The combine contract with skipped terms, from the oracle's own
+    arithmetic: a term whose row lies outside [0, cap) leaves acc as it is."""
+    T, k = pr.shape
+    acc = np.zeros((T, y.shape[1]), np.float32)
+    for j in range(k):
+        ok = (pr[:, j] >= 0) & (pr[:, j] < cap)
+        rows = oracle.bf16_to_f32(y[np.where(ok, pr[:, j], 0)])
+        acc = np.where(ok[:, None], oracle.fmaf(w[:, j][:, None], rows, acc), acc)
+    return oracle.f32_to_bf16_rne(acc)
+
+
+@pytest.mark.parametrize("T,H,k", [(37, 256, 8), (129, 1024, 3), (300, 512, 2), (64, 7168, 1),
+                                   (50, 640, 4), (5, 136, 12)])
+def test_combine_skips_terms_outside_the_buffer(T, H, k):
+    """Rows -1, -2^31, capacity, capacity + 7 and 2^31 - 1 in pair_row are
+    skipped terms (every combine kernel: fixed k = 1, 2, 4, 8 and any other
+    k); the rest of each token's chain is the oracle's."""
+    m = _m()
+    print(f"[edges] combine skipped terms T={T} H={H} k={k}", flush=True)
+    rng = np.random.default_rng(T * 7 + H + k)
+    P = T * k
+    cap = P + 2
+    pr = rng.permutation(cap)[:P].reshape(T, k).astype(np.int64)
+    bad = rng.random((T, k)) < 0.15
+    pr[bad] = rng.choice(np.array([-1, -(2 ** 31), cap, cap + 7, 2 ** 31 - 1]), int(bad.sum()))
+    pr[0, :] = -1                       # a token with every term skipped: +0
+    pr = pr.astype(np.int32)
+    y = _rand_bf16((cap, H), T + H)
+    w = rng.random((T, k)).astype(np.float32)
+    out = host_bf16(m.moe_combine(dev_bf16(y), dev_i32(pr), dev_f32(w), capacity=cap))
+    torch.cuda.synchronize()
+    ref = _combine_skipping(y, pr.astype(np.int64), w, cap)
+    assert (ref[0] == 0).all()
+    assert np.array_equal(out, ref)
