@@ -31,6 +31,7 @@ GRAPH_STEPS = 10                    # steps captured into one graph for graph_re
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", f"traffic_{TRAFFIC_WORKLOAD}.txt")
 VALU_FILE = os.path.join(ROOT, "profiles", f"valu_{TRAFFIC_WORKLOAD}.txt")
 TRACE_FILE = os.path.join(ROOT, "profiles", f"kernels_{TRAFFIC_WORKLOAD}.md")
+CEILING_FILE = os.path.join(ROOT, "profiles", "hbm_ceiling.md")
 # Where the timed launches find their inputs.
 CACHE_STATE = {
     "step": ("device memory; steps back to back, so x (read once per step) stays in the "
@@ -88,6 +89,38 @@ def measured_traffic(kernel: str, workload: str, cold: bool = False):
     (the launches after the cache flush when `cold`)."""
     return _committed_count(TRAFFIC_FILE, kernel, workload,
                             "kernels_cold" if cold else "kernels")
+
+
+def chip_ceilings():
+    """The chip's practical HBM rates from the committed probes.py
+    hbm_ceiling summary (TB/s: streaming read / write / copy, and reads and
+    writes of 1-16 KiB pieces in random order), or None without it."""
+    try:
+        with open(CEILING_FILE) as f:
+            return json.loads(f.read().split("JSON:", 1)[1].strip().splitlines()[0])
+    except (OSError, IndexError, ValueError):
+        return None
+
+
+def ceiling_bound(kernel: str, leg: str, cfg, ceil) -> dict:
+    """A row kernel's time if its reads and its writes each ran alone, one
+    after the other, at the chip's ceiling for their pattern, and the
+    fraction of the 8 TB/s peak that gives on its algorithmic bytes.  recv
+    reads each token row once, in order (streaming read; from the Infinity
+    Cache when warm, so not counted), and writes 2 KiB pieces of the k
+    destination rows at the expert segments (random-order writes).  Combine
+    gathers its k expert rows (random-order reads) and writes each output row
+    once, in order (streaming write)."""
+    T, H, P = cfg.T, cfg.H, cfg.P
+    if kernel == "dispatch_recv":
+        reads, writes = (2 * T * H, ceil["read_TBps"]), (2 * P * H + 4 * P, ceil["random_write_TBps"])
+        if leg == "warm":
+            reads = (0, reads[1])
+    else:
+        reads, writes = (2 * P * H + 8 * P, ceil["random_read_TBps"]), (2 * T * H, ceil["write_TBps"])
+    us = reads[0] / reads[1] / 1e6 + writes[0] / writes[1] / 1e6
+    nbytes = dict(algorithmic_bytes(cfg))[kernel]
+    return {"us": round(us, 2), "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
 def alu_roofline(kernel: str, us: float, workload: str):
@@ -587,6 +620,14 @@ def main() -> int:
             row_roof[n]["cold"] = {"us_mean": kernels_cold[n]["us_mean"],
                                    "GBps": kernels_cold[n]["GBps"],
                                    "frac": kernels_cold[n]["frac_of_peak"]}
+    ceil = chip_ceilings()
+    if ceil is not None:
+        for n in row_roof:
+            for lg in ("warm", "cold"):
+                if lg in row_roof[n]:
+                    b = ceiling_bound(n, lg, cfg, ceil)
+                    row_roof[n][lg]["chip_bound"] = dict(
+                        b, frac_of_bound=round(row_roof[n][lg]["frac"] / b["frac"], 4))
     leg = "cold" if kernels_cold else "warm"
     dom = max(["dispatch_recv", "combine"], key=lambda n: row_roof[n][leg]["us_mean"])
     if fp8 is not None:
@@ -638,6 +679,8 @@ def main() -> int:
             "unit": "GB/s",
             "frac": row_roof[dom][leg]["frac"],
             "traffic": traffic,
+            "chip_ceilings_TBps": ceil,
+            "chip_bound": row_roof[dom][leg].get("chip_bound"),
             "row_kernels": row_roof,
         },
         "kernels": kernels,

@@ -1,6 +1,6 @@
 """bench.py's host-side pieces (no GPU): the algorithmic byte counts the
-roofline uses, the counter-traffic and VALU-count lookups, and the one-GPU
-guard."""
+roofline uses, the counter-traffic and VALU-count lookups, the bound from
+the chip's measured ceilings, and the one-GPU guard."""
 import os
 import subprocess
 import sys
@@ -40,6 +40,27 @@ def test_alu_roofline_uses_the_committed_valu_count():
         cfg = workloads.CONFIGS[bench.TRAFFIC_WORKLOAD]
         # the routing kernel issues a few hundred VALU instructions per token
         assert 100 < got["valu_insts"] / cfg.T < 2000
+
+
+def test_chip_bound_from_the_committed_ceilings():
+    """Each row kernel's bound: its reads and writes one after the other at
+    the chip's measured ceilings for their pattern; recv's warm bound leaves
+    out the cache-resident x, so it is the tighter of recv's two."""
+    c = bench.chip_ceilings()
+    assert c is not None and set(c) >= {"read_TBps", "write_TBps", "random_write_TBps",
+                                        "random_read_TBps"}
+    assert c["random_write_TBps"] < c["write_TBps"] < c["read_TBps"] < 8.0
+    cfg = workloads.CONFIGS["dsv3_prefill"]
+    T, H, P = cfg.T, cfg.H, cfg.P
+    warm = bench.ceiling_bound("dispatch_recv", "warm", cfg, c)
+    cold = bench.ceiling_bound("dispatch_recv", "cold", cfg, c)
+    assert abs(warm["us"] - (2 * P * H + 4 * P) / c["random_write_TBps"] / 1e6) < 0.01
+    assert abs(cold["us"] - warm["us"] - 2 * T * H / c["read_TBps"] / 1e6) < 0.02
+    assert cold["frac"] < warm["frac"] < 1.0
+    comb = bench.ceiling_bound("combine", "cold", cfg, c)
+    assert comb == bench.ceiling_bound("combine", "warm", cfg, c)
+    want = (2 * P * H + 8 * P) / c["random_read_TBps"] / 1e6 + 2 * T * H / c["write_TBps"] / 1e6
+    assert abs(comb["us"] - want) < 0.01 and comb["frac"] < 1.0
 
 
 def test_more_than_one_gpu_is_refused():
