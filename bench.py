@@ -110,7 +110,9 @@ def ceiling_bound(kernel: str, leg: str, cfg, ceil) -> dict:
     Cache when warm, so not counted), and writes 2 KiB pieces of the k
     destination rows at the expert segments (random-order writes).  Combine
     gathers its k expert rows (random-order reads) and writes each output row
-    once, in order (streaming write)."""
+    once, in order (streaming write).  The random-order figure stands for
+    routing spread over many experts; a skewed routing writes more of its
+    rows in order and can beat it (frac_of_bound above 1)."""
     T, H, P = cfg.T, cfg.H, cfg.P
     if kernel == "dispatch_recv":
         reads, writes = (2 * T * H, ceil["read_TBps"]), (2 * P * H + 4 * P, ceil["random_write_TBps"])
