@@ -23,7 +23,9 @@
 //                        1-16 whole lanes.  Inside moe_route_dispatch
 //                        (E >= 128) the routing kernels also count each pair
 //                        into the send histogram with an atomic add, in
-//                        place of send_hist_kernel.
+//                        place of send_hist_kernel.  Below 128 experts,
+//                        route_topk_lds_count_kernel counts each 16-token
+//                        tile in LDS and adds the tile's bins instead.
 //   route_wave_kernel    one wave per token (small batches, and group-limited
 //                        routing the lane-group kernel cannot hold): k rounds
 //                        of a wave-wide maximum of the keys, the lowest
@@ -372,13 +374,15 @@ __device__ __forceinline__ void cache_push(uint32_t kv, int i, uint32_t (&h)[C],
 // rounds of a group maximum keep the best groups (ties to the lower group),
 // and the lanes of the other groups drop their keys before the k rounds.
 // The calling wave routes tokens t_wave .. t_wave + 64/G - 1 (t_wave < T).
-template <int G, int IPL, bool VEC, bool COUNT, bool GROUPED>
+// LDS (with COUNT): hist_mat is the calling block's LDS tile of matrix rows
+// row_first, row_first + 1, ...; the counts go there instead.
+template <int G, int IPL, bool VEC, bool COUNT, bool GROUPED, bool LDS = false>
 __device__ __forceinline__ void route_topk_tile(const float* __restrict__ logits, int64_t T,
                                                 int E, int k, int topk_group, int lg,
                                                 int32_t* __restrict__ topk_idx,
                                                 float* __restrict__ topk_w,
                                                 int32_t* __restrict__ hist_mat, uint32_t chunk,
-                                                int64_t t_wave) {
+                                                int64_t t_wave, uint32_t row_first = 0u) {
   constexpr int TPW = kWave / G;         // tokens per wave
   constexpr int C = IPL < 4 ? IPL : 4;   // cached candidates per lane
   const int lane = lane_id();
@@ -476,8 +480,11 @@ __device__ __forceinline__ void route_topk_tile(const float* __restrict__ logits
         idx_out[j] = e0 + ip;  // the owner reports winner j
         if constexpr (COUNT) {
           const uint32_t row = row0 + (rem0 + uint32_t(j) >= chunk ? 1u : 0u);
-          __hip_atomic_fetch_add(hist_mat + size_t(row) * E + e0 + ip, 1, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
+          if constexpr (LDS)
+            atomicAdd(hist_mat + (row - row_first) * uint32_t(E) + e0 + ip, 1);
+          else
+            __hip_atomic_fetch_add(hist_mat + size_t(row) * E + e0 + ip, 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
       }
       --rem;
@@ -531,6 +538,43 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
        t_wave < T; t_wave += stride)
     route_topk_tile<G, IPL, VEC, COUNT, GROUPED>(logits, T, E, k, topk_group, lg, topk_idx,
                                                  topk_w, hist_mat, chunk, t_wave);
+}
+
+// Counting routing for few experts (E < kRouteCountMinE), where one global
+// atomic per pair would pile onto too few addresses: each block routes tiles
+// of TPB tokens (one wave tile each) and counts the tile's pairs in LDS, one
+// bin per (matrix row, expert), then adds its nonzero bins to the matrix.
+// A tile's TPB * k <= 16 * 32 pairs span at most kRows rows (chunk >= 64).
+// The tile loop's bounds are the same for every wave of the block, so all of
+// them reach each barrier; a wave whose tile starts past T only counts in.
+template <int G, int IPL, bool VEC>
+__global__ __launch_bounds__(kRouteThreads) void route_topk_lds_count_kernel(
+    const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, int32_t* __restrict__ hist_mat, uint32_t chunk) {
+  constexpr int TPB = kRouteWavesPerBlock * (kWave / G);  // tokens per block tile
+  constexpr int kRows = (TPB * kMaxK + 63) / 64 + 1;
+  __shared__ int32_t bins[kRows * kRouteCountMinE];
+  const int wid = threadIdx.x / kWave;
+  const int64_t stride = int64_t(gridDim.x) * TPB;
+  for (int64_t t_block = int64_t(blockIdx.x) * TPB; t_block < T; t_block += stride) {
+    const int64_t t_end = t_block + TPB < T ? t_block + TPB : T;
+    const uint32_t row_first = uint32_t(t_block * k / chunk);
+    const int n = int(uint32_t((t_end * k - 1) / chunk) - row_first + 1) * E;
+    for (int i = threadIdx.x; i < n; i += kRouteThreads) bins[i] = 0;
+    __syncthreads();
+    const int64_t t_wave = t_block + int64_t(wid) * (kWave / G);
+    if (t_wave < T)
+      route_topk_tile<G, IPL, VEC, true, false, true>(logits, T, E, k, 1, 0, topk_idx, topk_w,
+                                                      bins, chunk, t_wave, row_first);
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += kRouteThreads) {
+      const int32_t c = bins[i];
+      if (c != 0)
+        __hip_atomic_fetch_add(hist_mat + size_t(row_first) * E + i, c, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();  // the next tile clears the bins
+  }
 }
 
 // One wave per token; IPL logits per lane (expert e = lane + 64 * i).  The
@@ -1720,6 +1764,38 @@ int enqueue_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t 
   return MOE_ERR_INVALID_ARG;  // unreachable: plan_route covers every E <= 1024, k <= 32
 }
 
+// Plain routing that also counts the send histogram matrix in LDS first
+// (route_topk_lds_count_kernel): for E < kRouteCountMinE in the lane-group
+// kernel's range with 16 lanes per token.  False: the plan does not fit, and
+// the caller counts with send_hist_kernel instead.
+bool route_lds_count_fits(int64_t T, int32_t E, int32_t k) {
+  return E < kRouteCountMinE && T > kRouteWaveMaxTokens && plan_route(T, E, k).G == 16;
+}
+
+int enqueue_route_lds_count(const float* logits, int64_t T, int32_t E, int32_t k,
+                            int32_t* topk_idx, float* topk_w, int32_t* hist_mat, int64_t chunk,
+                            hipStream_t s) {
+  const RoutePlan p = plan_route(T, E, k);
+  constexpr int TPB = kRouteWavesPerBlock * (kWave / 16);
+  const int64_t nb = (T + TPB - 1) / TPB;
+  const dim3 grid(unsigned(nb < kRouteMaxBlocks ? nb : kRouteMaxBlocks));
+  const dim3 block(kRouteThreads);
+  const bool vec = p.IPL % 4 == 0 && E % 4 == 0 && aligned(logits, 16);
+  const uint32_t ch = uint32_t(chunk);
+#define MOE_LDS_ROUTE(IPL_)                                                                  \
+  if (p.IPL == IPL_)                                                                         \
+    return vec ? launch(route_topk_lds_count_kernel<16, IPL_, (IPL_ % 4 == 0)>, grid, block, \
+                        0, s, logits, T, E, k, topk_idx, topk_w, hist_mat, ch)               \
+               : launch(route_topk_lds_count_kernel<16, IPL_, false>, grid, block, 0, s,     \
+                        logits, T, E, k, topk_idx, topk_w, hist_mat, ch);
+  MOE_LDS_ROUTE(1);
+  MOE_LDS_ROUTE(2);
+  MOE_LDS_ROUTE(4);
+  MOE_LDS_ROUTE(8);
+#undef MOE_LDS_ROUTE
+  return MOE_ERR_INVALID_ARG;  // unreachable: E < 128 gives IPL <= 8 at 16 lanes per token
+}
+
 int check_groups(int32_t E, int32_t k, int32_t n_group, int32_t topk_group) {
   if (n_group < 1 || n_group > kMaxGroups || E % n_group != 0) return MOE_ERR_INVALID_ARG;
   if (topk_group < 1 || topk_group > n_group || int64_t(topk_group) * (E / n_group) < k)
@@ -1972,9 +2048,13 @@ int enqueue_route_and_send(const float* logits, int64_t T, int32_t E, int32_t k,
   int32_t* mat = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kArrivalBytes);
   uint32_t* rank_arrivals = static_cast<uint32_t*>(workspace) + 1;
   const bool count = E >= kRouteCountMinE;
-  st = enqueue_route(logits, T, E, k, n_group, topk_group, topk_idx, topk_w, s,
-                     count ? mat : nullptr, plan.chunk);
-  if (st == MOE_OK && !count) st = enqueue_send_hist(topk_idx, T, E, k, mat, s);
+  if (!count && topk_group >= n_group && route_lds_count_fits(T, E, k)) {
+    st = enqueue_route_lds_count(logits, T, E, k, topk_idx, topk_w, mat, plan.chunk, s);
+  } else {
+    st = enqueue_route(logits, T, E, k, n_group, topk_group, topk_idx, topk_w, s,
+                       count ? mat : nullptr, plan.chunk);
+    if (st == MOE_OK && !count) st = enqueue_send_hist(topk_idx, T, E, k, mat, s);
+  }
   if (st != MOE_OK) return st;
   return enqueue_send_ranks(topk_idx, T, E, k, R, counts, offsets, pair_row, row_token,
                             rank_offsets, mat, rank_arrivals, s);

@@ -211,3 +211,34 @@ def test_grouped_route_dispatch_matches_separate_calls(T, E, k, G, TG, R):
     _same(got, (idx, w, send, buf))
     r_idx, _, _ = oracle.route_topk_grouped(lg, k, G, TG)
     assert np.array_equal(host(got[0]), r_idx)
+
+
+@pytest.mark.parametrize("T,E,k,R", [
+    (2049, 8, 3, 8),     # 48 pairs per 16-token tile: tiles straddle histogram rows
+    (5003, 100, 5, 4),   # odd E, ragged last tile
+    (2100, 127, 16, 1),  # the largest E below the threshold, k = 16: 256 pairs per tile
+    (9000, 2, 2, 2),
+    (5000, 1, 1, 1),     # one expert: every pair in one bin
+    (3000, 12, 7, 4),
+])
+def test_route_dispatch_counts_few_experts_in_lds(T, E, k, R):
+    """E < 128 with T above the one-wave-per-token routing and a multi-block
+    send: the routing kernel counts each 16-token tile's pairs in LDS and
+    adds them to the histogram matrix.  Against the separate calls and the
+    oracle, twice on one workspace, which is zero after each call."""
+    m = _m()
+    print(f"[route_dispatch] lds counting T={T} E={E} k={k} R={R}", flush=True)
+    lg, xb = _inputs(T, E, 64, T * 3 + E + k)
+    logits, x = dev_f32(lg), dev_bf16(xb)
+    ws = torch.zeros((m.moe_route_dispatch_workspace_bytes(T, E, k),), dtype=torch.uint8,
+                     device=DEV)
+    ref = _separate(m, logits, x, k, E, R)
+    for _ in range(2):
+        got = m.moe_route_dispatch(logits, x, k, R, workspace=ws)
+        torch.cuda.synchronize()
+        _same(got, ref)
+        assert int(ws.count_nonzero().item()) == 0
+    r_idx, _, _ = oracle.route_topk(lg, k)
+    assert np.array_equal(host(got[0]), r_idx)
+    pr, _ = oracle.dispatch_slots(r_idx, E)
+    assert np.array_equal(host(got[2].pair_row), pr)
