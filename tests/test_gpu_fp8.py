@@ -90,7 +90,8 @@ def test_fp8_chain_matches_oracle():
 
 @pytest.mark.parametrize("T,E,k,R,H,G,TG", [
     (16, 8, 2, 1, 256, 1, 1),          # one launch for route + send
-    (128, 256, 8, 32, 7168, 1, 1),     # DSv3 decode shape
+    (128, 256, 8, 32, 7168, 1, 1),     # DSv3 decode shape: routing, then send + fp8 recv in one launch
+    (128, 256, 8, 32, 7168, 8, 4),     # the same with group-limited routing
     (300, 384, 8, 48, 1024, 8, 4),     # group-limited, 16-wave single-block send
     (3000, 64, 4, 8, 512, 1, 1),       # lane-group routing, histogram kernel (E < 128)
     (4096, 256, 8, 32, 2048, 1, 1),    # routing that counts the send histogram
