@@ -1765,11 +1765,12 @@ int enqueue_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t 
 }
 
 // Plain routing that also counts the send histogram matrix in LDS first
-// (route_topk_lds_count_kernel): for E < kRouteCountMinE in the lane-group
-// kernel's range with 16 lanes per token.  False: the plan does not fit, and
-// the caller counts with send_hist_kernel instead.
+// (route_topk_lds_count_kernel): for E < kRouteCountMinE with 16 lanes per
+// token, at any T (below 2049 tokens it takes the place of the one wave per
+// token kernel, and is faster than that kernel plus send_hist_kernel).
+// False: the plan does not fit, and the caller counts with send_hist_kernel.
 bool route_lds_count_fits(int64_t T, int32_t E, int32_t k) {
-  return E < kRouteCountMinE && T > kRouteWaveMaxTokens && plan_route(T, E, k).G == 16;
+  return E < kRouteCountMinE && plan_route(T, E, k).G == 16;
 }
 
 int enqueue_route_lds_count(const float* logits, int64_t T, int32_t E, int32_t k,

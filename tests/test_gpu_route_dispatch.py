@@ -220,12 +220,14 @@ def test_grouped_route_dispatch_matches_separate_calls(T, E, k, G, TG, R):
     (9000, 2, 2, 2),
     (5000, 1, 1, 1),     # one expert: every pair in one bin
     (3000, 12, 7, 4),
+    (1100, 64, 4, 8),    # below 2049 tokens: the lane-group kernel routes these too
+    (1025, 8, 8, 1),     # P = 8200, ragged last tile
 ])
 def test_route_dispatch_counts_few_experts_in_lds(T, E, k, R):
-    """E < 128 with T above the one-wave-per-token routing and a multi-block
-    send: the routing kernel counts each 16-token tile's pairs in LDS and
-    adds them to the histogram matrix.  Against the separate calls and the
-    oracle, twice on one workspace, which is zero after each call."""
+    """E < 128 with a multi-block send: the lane-group routing kernel counts
+    each 16-token tile's pairs in LDS and adds them to the histogram matrix.
+    Against the separate calls and the oracle, twice on one workspace, which
+    is zero after each call."""
     m = _m()
     print(f"[route_dispatch] lds counting T={T} E={E} k={k} R={R}", flush=True)
     lg, xb = _inputs(T, E, 64, T * 3 + E + k)
