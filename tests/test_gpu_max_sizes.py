@@ -5,7 +5,8 @@
   token tiles; send runs 64 blocks of 2^25 pairs; recv and combine run
   2^30 row units through their capped grids.
 * The one-call path (route, send, recv) at T*k = 2^31 - 32 with E = 128,
-  where the routing kernel counts the send histogram.
+  where the routing kernel counts the send histogram, and with E = 8 at
+  T = 2^24 + 37, where it counts per tile in LDS past its 2^20-block grid.
 * Group-limited routing with 64*T past 2^32 (one wave per token, looping).
 * Row offsets past 2^31 16-byte units (H = 8192, T = 2^21 + 3): recv,
   combine and the fp8 recv address bytes beyond 2^35.
@@ -221,6 +222,43 @@ def test_one_call_path_at_the_pair_limit():
         _check_topk_rows(logits[t0:t0 + n], idx[t0:t0 + n])
         assert bool(torch.isfinite(w[t0:t0 + n]).all())
     s = _sample(T, 2048, 4)
+    st = torch.from_numpy(s).to(DEV)
+    r_idx, r_w, _ = oracle.route_topk(host(logits[st]), k)
+    assert np.array_equal(host(idx[st]), r_idx)
+    assert_weights_close(host(w[st]), r_w)
+    del logits
+    _check_slots(idx.view(-1), E, k, send)
+    assert torch.equal(send.rank_offsets.long(), send.expert_offsets.long()[::E // R])
+    _check_rows(buf, x, send.row_token)
+
+
+def test_lds_counting_route_past_its_grid():
+    """moe_route_dispatch with E = 8, where the routing kernel counts each
+    16-token tile's pairs in LDS, at T = 2^24 + 37: its 2^20 blocks take a
+    second tile where there is one (the last one ragged), tiles straddle
+    histogram rows, and the rank kernel reads and clears the matrix.  Two
+    calls on one workspace, which is zero after each."""
+    import combine_topk_route_amd as m
+
+    T, E, k, R, H = (1 << 24) + 37, 8, 2, 2, 8
+    _say(f"route_dispatch (LDS counting) T={T} E={E} k={k} R={R} H={H}")
+    g = torch.Generator(device=DEV).manual_seed(24)
+    logits = _randn((T, E), g)
+    x = _randn((T, H), g, torch.bfloat16)
+    ws = torch.zeros((m.moe_route_dispatch_workspace_bytes(T, E, k),), dtype=torch.uint8,
+                     device=DEV)
+    idx = _full((T, k), -1, torch.int32)
+    w = _full((T, k), float("nan"), torch.float32)
+    for _ in range(2):
+        idx, w, send, buf = m.moe_route_dispatch(logits, x, k, R, topk_idx=idx, topk_w=w,
+                                                 workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero().item()) == 0
+    n = _step(E)
+    for t0 in range(0, T, n):
+        _check_topk_rows(logits[t0:t0 + n], idx[t0:t0 + n])
+        assert bool(torch.isfinite(w[t0:t0 + n]).all())
+    s = _sample(T, 2048, 5)
     st = torch.from_numpy(s).to(DEV)
     r_idx, r_w, _ = oracle.route_topk(host(logits[st]), k)
     assert np.array_equal(host(idx[st]), r_idx)
