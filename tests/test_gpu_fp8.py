@@ -192,3 +192,28 @@ def test_fp8_dispatch_in_one_launch_matches_send_then_recv(T, k, E, R, H, drops)
         eq, es = oracle.dispatch_rows_fp8(x, r_pr, cap, np.full((cap, H), 0x5A, np.uint8),
                                           np.full((cap, H // 128), -2.0, np.float32))
         assert np.array_equal(qa, eq) and np.array_equal(sa.view(np.uint32), es.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["tiny", "dsv3_decode"])
+def test_fp8_one_call_on_the_small_workloads(name):
+    """moe_route_dispatch_fp8 on the seeded workloads whose T*k <= 2048
+    (routing, then send + fp8 recv in one launch), against the oracle:
+    indices, slots, codes and scales bit-exact, weights within 2^-20."""
+    import combine_topk_route_amd as m
+    from gpuhelp import assert_weights_close, dev_f32
+
+    wl = workloads.make(name, seed=4, with_y=False)
+    cfg = wl.cfg
+    assert cfg.T * cfg.k <= 2048
+    print(f"[fp8] one call {name} T={cfg.T} E={cfg.E} k={cfg.k} H={cfg.H}", flush=True)
+    idx, w, send, q, s = m.moe_route_dispatch_fp8(dev_f32(wl.logits), dev_bf16(wl.x), cfg.k, cfg.R)
+    torch.cuda.synchronize()
+    r_idx, r_w, _ = oracle.route_topk(wl.logits, cfg.k)
+    assert np.array_equal(host(idx), r_idx)
+    assert_weights_close(host(w), r_w)
+    pr, rt = oracle.dispatch_slots(r_idx, cfg.E)
+    assert np.array_equal(host(send.pair_row), pr)
+    assert np.array_equal(host(send.row_token), rt)
+    rq, rs = oracle.dispatch_rows_fp8(wl.x, pr, cfg.P)
+    assert np.array_equal(host(q), rq)
+    assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32))
