@@ -2,7 +2,8 @@
 (moe_route_dispatch, then moe_combine) against the oracle: batch sizes on
 both sides of every launch-plan switch (one launch for route and send, the
 single-block and multi-block sends, one wave per token and lane groups, the
-routing kernel counting the send histogram or not), expert counts from 1 to
+routing kernel counting the send histogram with global atomics, per tile in
+LDS, or not at all), expert counts from 1 to
 1024, odd widths, plain and group-limited routing.  One workspace serves
 every call and must be all zeros after each.  Bars: indices, counts,
 offsets, slots and rows bit-exact; weights within 2^-20; combine of the
@@ -49,8 +50,8 @@ def _cases(n=48, seed=2026):
 
 # Large batches that the draw above rarely reaches: lane-group routing that
 # counts the send histogram (E >= 128), multi-step waves in the rank kernel
-# (E = 1024, k = 32: 16 blocks of 16384 pairs), and the histogram kernel
-# below the counting threshold.
+# (E = 1024, k = 32: 16 blocks of 16384 pairs), and the per-tile LDS counts
+# below 128 experts.
 EXTRA = [(4097, 256, 8, 32, 8, 1, 1), (6000, 384, 8, 48, 8, 1, 1), (4097, 1024, 8, 32, 8, 1, 1),
          (3000, 128, 16, 16, 64, 1, 1), (6000, 513, 5, 27, 8, 1, 1),
          (8192, 1024, 32, 32, 8, 1, 1), (5000, 100, 8, 4, 8, 1, 1),
